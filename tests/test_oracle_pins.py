@@ -1,0 +1,399 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks the oracle against a hand-derived fixture, a library routine
+(numpy's stable sort, torch's float8/bfloat16 casts), a closed form, an
+invariant or brute force on tiny inputs.  Together they are chosen so that a
+plausible slip in the oracle (a dropped term, a wrong sign, index or operand,
+a wrong tie rule) fails at least one of them.
+"""
+import json
+import os
+from concurrent.futures import ThreadPoolExecutor
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_ep_layout_02_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# layout
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", _golden("layout_hand.json")["cases"], ids=lambda c: c["name"])
+def test_layout_hand_fixture(case):
+    lay = oracle.layout(np.array(case["topk_idx"], np.int32), case["E"], case["R"],
+                        case["A"], case["C"])
+    assert lay.expert_count.tolist() == case["expert_count"]
+    assert lay.expert_offset.tolist() == case["expert_offset"]
+    assert lay.rank_count.tolist() == case["rank_count"]
+    assert lay.rank_offset.tolist() == case["rank_offset"]
+    assert lay.slot.tolist() == case["slot"]
+    assert lay.src_pair.tolist() == case["src_pair"]
+    assert lay.diag.tolist() == case["diag"]
+
+
+def _random_idx(rng, T, k, E, mask_frac=0.0, bad_frac=0.0):
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32) if T else \
+        np.zeros((0, k), np.int32)
+    if mask_frac:
+        idx[rng.random(idx.shape) < mask_frac] = -1
+    if bad_frac:
+        bad = rng.random(idx.shape) < bad_frac
+        idx[bad] = rng.choice([-7, -2, E, E + 3], size=int(bad.sum()))
+    return idx
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "v3", "decode", "skew"])
+def test_layout_counts_offsets_sort_on_workloads(name):
+    w = wl.WORKLOADS[name]
+    idx, _ = wl.make_routing(w)
+    lay = oracle.layout(idx, w.num_experts, w.num_ranks, w.expert_alignment, w.capacity)
+    E, T, k = w.num_experts, w.num_tokens, w.num_topk
+    cnt = np.bincount(idx.ravel(), minlength=E)
+    assert np.array_equal(lay.expert_count, cnt)
+    assert lay.expert_count.sum() == T * k
+    if w.capacity:
+        assert np.array_equal(lay.expert_offset, np.arange(E + 1) * w.capacity)
+        assert (cnt <= w.capacity).all() and lay.diag[1] == 0
+        pos = lay.slot - idx * w.capacity
+        assert ((pos >= 0) & (pos < w.capacity)).all()
+    else:
+        assert np.array_equal(lay.expert_offset, np.concatenate([[0], np.cumsum(cnt)]))
+        # a stable counting sort of the pairs by expert id is numpy's stable argsort
+        assert np.array_equal(lay.src_pair, np.argsort(idx.ravel(), kind="stable"))
+    # rank bookkeeping against per-token sets
+    per = E // w.num_ranks
+    want = np.zeros(w.num_ranks, np.int64)
+    for row in idx:
+        for r in set((row // per).tolist()):
+            want[r] += 1
+    assert np.array_equal(lay.rank_count, want)
+    assert np.array_equal(lay.rank_offset, lay.expert_offset[::per])
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("A,C", [(1, 0), (4, 0), (1, 3), (1, 64)])
+def test_layout_invariants_random(seed, A, C):
+    rng = np.random.default_rng(100 + seed)
+    T, E, R = int(rng.integers(0, 60)), 16, 4
+    k = int(rng.integers(1, 6))
+    idx = _random_idx(rng, T, k, E, mask_frac=0.1, bad_frac=0.05)
+    lay = oracle.layout(idx, E, R, A, C)
+    valid = (idx >= 0) & (idx < E)
+    assert lay.diag[0] == int(((idx != -1) & ~valid).sum())
+    assert np.array_equal(lay.expert_count, np.bincount(idx[valid], minlength=E))
+    flat = lay.slot.ravel()
+    held = np.flatnonzero(lay.src_pair >= 0)
+    # every row that holds a pair points back at it, and vice versa
+    assert np.array_equal(flat[lay.src_pair[held]], held)
+    assert np.array_equal(np.sort(lay.src_pair[held]), np.flatnonzero(flat >= 0))
+    dropped = valid.ravel() & (flat < 0)
+    assert lay.diag[1] == int(dropped.sum())
+    if C == 0:
+        assert not dropped.any()
+    ev = idx.ravel()
+    for p in np.flatnonzero(flat >= 0):
+        e = ev[p]
+        assert lay.expert_offset[e] <= flat[p] < lay.expert_offset[e + 1]
+    # slots within one expert rise with the pair index (stable order)
+    for e in range(E):
+        ps = np.flatnonzero((ev == e) & (flat >= 0))
+        assert np.all(np.diff(flat[ps]) == 1)
+        assert len(ps) == 0 or flat[ps[0]] == lay.expert_offset[e]
+    if C == 0:
+        seg = np.diff(lay.expert_offset)
+        assert np.all(seg % A == 0) and np.all(seg - lay.expert_count < A)
+        assert np.all(seg >= lay.expert_count)
+    else:
+        assert np.array_equal(lay.expert_offset, np.arange(E + 1) * C)
+        assert np.array_equal(np.minimum(lay.expert_count, C),
+                              np.bincount(ev[flat >= 0], minlength=E))
+
+
+def test_layout_each_token_appears_k_times():
+    w = wl.WORKLOADS["v3"]
+    idx, _ = wl.make_routing(w)
+    lay = oracle.layout(idx, w.num_experts, w.num_ranks)
+    tok = lay.src_pair // w.num_topk
+    assert np.array_equal(np.bincount(tok, minlength=w.num_tokens),
+                          np.full(w.num_tokens, w.num_topk))
+
+
+def test_layout_empty_batch():
+    lay = oracle.layout(np.zeros((0, 4), np.int32), 8, 2, 3, 0)
+    assert lay.expert_count.tolist() == [0] * 8
+    assert lay.expert_offset.tolist() == [0] * 9
+    assert lay.src_pair.tolist() == [-1] * 16  # E*(A-1) worst-case padding rows
+    lay = oracle.layout(np.zeros((0, 4), np.int32), 8, 2, 1, 5)
+    assert lay.expert_offset.tolist() == list(range(0, 45, 5))
+    assert (lay.src_pair == -1).all() and lay.src_pair.size == 40
+
+
+# --------------------------------------------------------------------------
+# number formats
+# --------------------------------------------------------------------------
+
+def _torch_e4m3(v: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+
+
+def test_e4m3_decode_matches_torch_for_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e4m3_decode(codes)
+    theirs = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(theirs)
+    assert nan.tolist() == [c in (0x7F, 0xFF) for c in range(256)]
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], theirs[~nan])
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+
+
+def test_e4m3_roundtrip_all_finite_codes():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    vals = oracle.e4m3_decode(codes).astype(np.float32)
+    vals[codes == 0x80] = np.float32(-0.0)
+    assert np.array_equal(oracle.e4m3_encode(vals), codes)
+
+
+def test_e4m3_encode_brute_force_nearest():
+    """Nearest code by exhaustive search over the 127 magnitudes, ties to even mantissa."""
+    mags = [Fraction(m, 512) if (c >> 3) == 0 else Fraction(8 + m) * Fraction(2) ** ((c >> 3) - 10)
+            for c in range(127) for m in [c & 7]]
+    rng = np.random.default_rng(7)
+    v = np.concatenate([rng.standard_normal(3000).astype(np.float32) * s
+                        for s in (1e-3, 0.05, 1.0, 30.0, 200.0)])
+    got = oracle.e4m3_encode(v)
+    for x, g in zip(v.tolist(), got.tolist()):
+        a = Fraction(abs(x))
+        if a >= 448:
+            want = 0x7E
+        else:
+            d = [abs(a - m) for m in mags]
+            best = min(d)
+            cands = [c for c in range(127) if d[c] == best]
+            want = cands[0] if len(cands) == 1 else [c for c in cands if c % 2 == 0][0]
+        want |= 0x80 if np.signbit(np.float32(x)) else 0
+        assert g == want, (x, hex(g), hex(want))
+
+
+def _boundary_values():
+    """Every code value and every midpoint between adjacent codes, +-3 float32 ulps."""
+    mags = oracle.e4m3_decode(np.arange(127, dtype=np.uint8))
+    pts = np.concatenate([mags, (mags[:-1] + mags[1:]) / 2, [448.0, 456.0, 464.0]]).astype(np.float32)
+    bits = pts.view(np.uint32).astype(np.int64)
+    near = (bits[:, None] + np.arange(-3, 4)[None, :]).ravel()
+    near = near[(near >= 0) & (near < 0x7F800000)].astype(np.uint32).view(np.float32)
+    near = near[near <= 464.0]
+    return np.concatenate([near, -near])
+
+
+def test_e4m3_encode_matches_torch_at_every_rounding_boundary():
+    v = _boundary_values()
+    assert np.array_equal(oracle.e4m3_encode(v), _torch_e4m3(v))
+
+
+def test_e4m3_encode_specials():
+    enc = oracle.lib().oracle_e4m3_encode
+    assert enc(448.00003) == 0x7E          # quotient just above 448
+    assert enc(464.0) == 0x7E              # midpoint 448/480 -> even (448)
+    assert enc(1e6) == 0x7E and enc(-1e6) == 0xFE  # saturation
+    assert enc(-0.0) == 0x80 and enc(0.0) == 0x00
+    assert enc(3 * 2.0 ** -10) == 0x02
+    assert enc(float("nan")) == 0x7F
+
+
+@pytest.mark.slow
+def test_e4m3_encode_matches_torch_strided_sweep():
+    """Every 61st float32 bit pattern in [-464, 464] (about 37M values)."""
+    top = int(np.array([464.0], np.float32).view(np.uint32)[0])
+
+    def chunk(lo):
+        b = np.arange(lo, min(lo + (1 << 26), top + 1), 61, dtype=np.uint32)
+        v = b.view(np.float32)
+        v = np.concatenate([v, -v])
+        return int((oracle.e4m3_encode(v) != _torch_e4m3(v)).sum())
+
+    with ThreadPoolExecutor(8) as ex:
+        bad = sum(ex.map(chunk, range(0, top + 1, 1 << 26)))
+    assert bad == 0
+
+
+def test_bf16_rne_matches_torch():
+    rng = np.random.default_rng(3)
+    v = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32),
+        (rng.standard_normal(20000) * 1e-38).astype(np.float32),   # subnormals
+        np.array([3.3895314e38, 3.4028235e38, -3.4028235e38, 0.0, -0.0], np.float32),
+    ])
+    # exact ties: low 16 bits = 0x8000 with either parity of bit 16
+    ties = ((rng.integers(0, 1 << 15, 5000, dtype=np.uint32) << 17)
+            | (rng.integers(0, 2, 5000, dtype=np.uint32) << 16) | 0x8000).view(np.float32)
+    ties = ties[np.isfinite(ties)]
+    v = np.concatenate([v, ties])
+    want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.bf16_rne(v), want)
+
+
+# --------------------------------------------------------------------------
+# dispatch
+# --------------------------------------------------------------------------
+
+def _f32(x):
+    return np.float32(-0.0) if x == "-0.0" else np.float32(x)
+
+
+def test_fp8_dispatch_hand_fixture():
+    g = _golden("fp8_block_hand.json")
+    H = g["hidden"]
+    xf = np.zeros(H, np.float32)
+    for i, v, _ in g["block0_nonzero"]:
+        xf[i] = _f32(v)
+    x = wl.f32_to_bf16_bits(xf)[None, :]
+    assert np.array_equal(wl.bf16_bits_to_f32(x)[0], xf)  # all inputs are BF16-exact
+    slot = np.array([[1, 0]], np.int32)
+    q, s = oracle.dispatch_fp8(x, slot, 2)
+    want = np.zeros(H, np.uint8)
+    for i, _, c in g["block0_nonzero"]:
+        want[i] = int(c, 16)
+    for row in (0, 1):
+        assert q[row].tolist() == want.tolist()
+        assert s[row, 0] == np.float32(g["block0_scale"])
+        assert s[row, 1] == np.float32(np.float32(1e-4) / np.float32(448.0))
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_fp8_dispatch_error_bound_and_copies(name):
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w, with_y=False)
+    lay = oracle.layout(inp.topk_idx, w.num_experts, w.num_ranks, w.expert_alignment, w.capacity)
+    rows = w.recv_rows
+    q, s = oracle.dispatch_fp8(inp.x, lay.slot, rows)
+    xf = wl.bf16_bits_to_f32(inp.x).astype(np.float64)
+    T, H, k = w.num_tokens, w.hidden, w.num_topk
+    for t in range(T):
+        sl = lay.slot[t]
+        sl = sl[sl >= 0]
+        assert len(sl) == k
+        for r in sl[1:]:
+            assert np.array_equal(q[r], q[sl[0]]) and np.array_equal(s[r], s[sl[0]])
+        r = sl[0]
+        dq = oracle.e4m3_decode(q[r]).reshape(H // 128, 128)
+        sc = s[r].astype(np.float64)[:, None]
+        xb = xf[t].reshape(H // 128, 128)
+        err = np.abs(xb - dq * sc)
+        bound = np.maximum(2.0 ** -4 * np.abs(xb), 2.0 ** -10 * sc) * (1 + 2.0 ** -20)
+        assert (err <= bound).all()
+        # the largest |x| of each block lands on the largest code
+        amax_pos = np.abs(xb).argmax(axis=1)
+        top = q[r].reshape(H // 128, 128)[np.arange(H // 128), amax_pos]
+        assert np.all((top & 0x7F) == 0x7E)
+        want_s = np.maximum(np.abs(xb).max(axis=1).astype(np.float32), np.float32(1e-4)) / np.float32(448)
+        assert np.array_equal(s[r], want_s.astype(np.float32))
+
+
+def test_bf16_dispatch_copies_rows():
+    w = wl.WORKLOADS["tiny"]
+    inp = wl.make_inputs(w, with_y=False)
+    lay = oracle.layout(inp.topk_idx, w.num_experts, w.num_ranks)
+    rx = oracle.dispatch_bf16(inp.x, lay.slot, w.recv_rows)
+    for t in range(w.num_tokens):
+        for r in lay.slot[t]:
+            assert np.array_equal(rx[r], inp.x[t])
+    assert np.array_equal(rx, inp.x[lay.src_pair // w.num_topk])
+
+
+# --------------------------------------------------------------------------
+# combine
+# --------------------------------------------------------------------------
+
+def test_combine_hand_fixture():
+    g = _golden("combine_hand.json")
+    y = wl.f32_to_bf16_bits(np.array(g["y"], np.float32))
+    out = oracle.combine(y, np.array(g["slot"], np.int32), np.array(g["weights"], np.float32))
+    want = [[int(b, 16) for b in row] for row in g["out_bits"]]
+    assert out.tolist() == want
+
+
+def test_combine_k1_unit_weight_is_gather():
+    rng = np.random.default_rng(11)
+    y = wl.normal_bf16(11, 2, 50, 64)
+    slot = rng.permutation(50)[:40].astype(np.int32)[:, None]
+    out = oracle.combine(y, slot, np.ones((40, 1), np.float32))
+    assert np.array_equal(out, y[slot[:, 0]])
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_combine_of_dispatch_is_identity(name):
+    """BF16 dispatch, experts = identity, weights summing to 1: combine returns x."""
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w, with_y=False)
+    lay = oracle.layout(inp.topk_idx, w.num_experts, w.num_ranks, 1, w.capacity)
+    assert np.abs(inp.topk_weights.astype(np.float64).sum(1) - 1).max() < 2.0 ** -20
+    rx = oracle.dispatch_bf16(inp.x, lay.slot, w.recv_rows)
+    out = oracle.combine(rx, lay.slot, inp.topk_weights)
+    assert np.array_equal(out, inp.x)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid"])
+def test_combine_within_fp32_error_bound_of_exact_sum(name):
+    """|out - sum_j w*y| <= half a BF16 ulp of out + k * 2^-24 * sum_j |w*y| (fp64 reference)."""
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w)
+    lay = oracle.layout(inp.topk_idx, w.num_experts, w.num_ranks)
+    T = min(w.num_tokens, 512)
+    out = oracle.combine(inp.y, lay.slot[:T], inp.topk_weights[:T])
+    yf = wl.bf16_bits_to_f32(inp.y).astype(np.float64)
+    terms = inp.topk_weights[:T, :, None].astype(np.float64) * yf[lay.slot[:T]]
+    exact = terms.sum(1)
+    mag = np.abs(terms).sum(1)
+    of = wl.bf16_bits_to_f32(out).astype(np.float64)
+    half_ulp = np.ldexp(1.0, np.frexp(np.abs(of))[1] - 9)
+    bound = half_ulp + w.num_topk * 2.0 ** -24 * mag + 1e-45
+    assert (np.abs(of - exact) <= bound).all()
+    # and the bound is not vacuous: most outputs are the correctly rounded exact sum
+    assert (out == oracle.bf16_rne(exact.astype(np.float32))).mean() > 0.99
+
+
+def test_combine_skips_masked_slots():
+    y = wl.normal_bf16(12, 2, 8, 32)
+    slot = np.array([[3, -1, 5], [-1, -1, -1]], np.int32)
+    wts = np.array([[0.5, 100.0, 0.25], [1.0, 1.0, 1.0]], np.float32)
+    out = oracle.combine(y, slot, wts)
+    yf = wl.bf16_bits_to_f32(y)
+    want0 = oracle.bf16_rne(np.float32(0.5) * yf[3] + np.float32(0.25) * yf[5])
+    assert np.array_equal(out[0], want0)
+    assert (out[1] == 0).all()
+
+
+# --------------------------------------------------------------------------
+# generators
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "v3", "decode", "skew"])
+def test_generators(name):
+    w = wl.WORKLOADS[name]
+    idx, wts = wl.make_routing(w)
+    idx2, wts2 = wl.make_routing(w)
+    assert np.array_equal(idx, idx2) and np.array_equal(wts, wts2)
+    assert idx.shape == (w.num_tokens, w.num_topk) and idx.dtype == np.int32
+    assert all(len(set(r)) == w.num_topk for r in idx.tolist())
+    assert ((idx >= 0) & (idx < w.num_experts)).all()
+    assert np.abs(wts.astype(np.float64).sum(1) - 1).max() < 1e-6 and (wts > 0).all()
+    if w.routing == "group_limited":
+        gsz = w.num_experts // w.num_groups
+        assert max(len(set((r // gsz).tolist())) for r in idx) <= w.topk_groups
+    if w.zipf_alpha:
+        frac = np.bincount(idx.ravel(), minlength=w.num_experts) / w.num_tokens
+        assert 1 <= (frac > 0.10).sum() <= 12

@@ -1,0 +1,257 @@
+"""Throughput of the MoE layout -> dispatch -> combine path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is the whole path over one batch of the 8K-token workload
+(T=8192 tokens, hidden 7168, 256 experts in 8 ranks, top-8 group-limited
+routing): ep_layout, FP8 E4M3 1x128 ep_dispatch and BF16 ep_combine, all on
+one HIP stream with every input already resident in HBM.  The headline value
+is algorithmic bytes per step (layout + dispatch + combine, counted as the
+method must move them) times K over the wall time of K steps.
+
+Also reported: per-stage kernel times from HIP events recorded around each
+stage inside the timed loop, the roofline of the dominant kernel (combine,
+HBM-bound), the decode-shaped workload's microseconds per call, and the CPU
+oracle timed on this host (one thread) on the same workload.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import combine_ep_layout_02_amd as ep  # noqa: E402
+from combine_ep_layout_02_amd import ep as epmod  # noqa: E402
+from combine_ep_layout_02_amd import workloads as wl  # noqa: E402
+
+METRIC = "dispatch+combine HBM GB/s & % peak at 8K tok,h7168,top-8; decode µs/call"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_v3_traffic.json")
+KERNEL_SOURCES = ["combine_ep_layout_02_amd/csrc/ep_combine.hip", "combine_ep_layout_02_amd/csrc/ep_device.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------
+# algorithmic bytes (what the method must move)
+# --------------------------------------------------------------------------
+
+def bytes_layout(w):
+    return 8 * w.num_tokens * w.num_topk + 4 * w.recv_rows
+
+
+def bytes_dispatch(w, fp8):
+    T, H, k = w.num_tokens, w.hidden, w.num_topk
+    if fp8:
+        return 2 * T * H + 4 * T * k + T * k * H + 4 * T * k * (H // 128)
+    return 2 * T * H + 4 * T * k + 2 * T * k * H
+
+
+def bytes_combine(w):
+    T, H, k = w.num_tokens, w.hidden, w.num_topk
+    return 2 * T * k * H + 8 * T * k + 2 * T * H
+
+
+# --------------------------------------------------------------------------
+# device setup
+# --------------------------------------------------------------------------
+
+class Step:
+    """Device buffers of one workload and the three calls of one step."""
+
+    def __init__(self, w, dev, fp8=True):
+        self.w, self.fp8 = w, fp8
+        self.shape = ep.EpShape(w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks,
+                                w.expert_alignment, w.capacity)
+        inp = wl.make_inputs(w)
+        self.inp = inp
+        self.idx = torch.from_numpy(inp.topk_idx).to(dev)
+        self.wts = torch.from_numpy(inp.topk_weights).to(dev)
+        self.x = torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.y = torch.from_numpy(inp.y.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.lay = ep.LayoutBuffers.allocate(self.shape, dev)
+        self.dtype = ep.EP_FP8_E4M3 if fp8 else ep.EP_BF16
+        self.recv_x, self.recv_scale = ep.alloc_recv(self.shape, self.dtype, dev)
+        self.out = torch.empty_like(self.x)
+
+    def layout(self):
+        self.lay.run(self.idx)
+
+    def dispatch(self):
+        ep.ep_dispatch(self.shape, self.x, self.lay.slot, self.dtype, self.recv_x, self.recv_scale)
+
+    def combine(self):
+        ep.ep_combine(self.shape, self.y, self.lay.slot, self.wts, self.out)
+
+    def run(self):
+        self.layout()
+        self.dispatch()
+        self.combine()
+
+    @property
+    def bytes(self):
+        return bytes_layout(self.w) + bytes_dispatch(self.w, self.fp8) + bytes_combine(self.w)
+
+
+def time_steps(step, steps, warmup):
+    """Warm up, then time `steps` steps with per-stage events on the launch stream."""
+    for _ in range(warmup):
+        step.run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        e = ev[i]
+        e[0].record()
+        step.layout()
+        e[1].record()
+        step.dispatch()
+        e[2].record()
+        step.combine()
+        e[3].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])  # ms
+    return total_ms, wall, stage
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per combine launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# --------------------------------------------------------------------------
+# CPU oracle baseline
+# --------------------------------------------------------------------------
+
+def cpu_baseline(step):
+    import oracle  # test infrastructure; only this leg of the benchmark uses it
+    w, inp = step.w, step.inp
+    times = []
+    for _ in range(2):
+        t0 = time.perf_counter()
+        lay = oracle.layout(inp.topk_idx, w.num_experts, w.num_ranks, w.expert_alignment, w.capacity)
+        oracle.dispatch_fp8(inp.x, lay.slot, w.recv_rows)
+        oracle.combine(inp.y, lay.slot, inp.topk_weights)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"value": round(step.bytes / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the full {w.name} step (layout + FP8 dispatch + combine of {w.num_tokens} tokens), "
+                      f"median of 2 runs, {t:.2f} s each, single-threaded C on the host"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="v3", choices=["v3", "skew"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU's share of the path; it has no multi-GPU mode "
+              "(the ranks are segments of one HBM buffer). Run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not os.path.exists(epmod.library_path()):
+        from combine_ep_layout_02_amd.build import build_library
+        build_library()
+    dev = torch.device("cuda:0")
+
+    w = wl.WORKLOADS[args.workload]
+    log(f"[bench] generating {w.name} inputs")
+    step = Step(w, dev, fp8=True)
+    log(f"[bench] timing {args.steps} steps after {args.warmup} warm-up")
+    total_ms, wall, stage = time_steps(step, args.steps, args.warmup)
+    ms_per_step = total_ms / args.steps
+    value = step.bytes * args.steps / (total_ms / 1e3) / 1e9
+    lay_ms, disp_ms, comb_ms = stage.mean(axis=0)
+
+    dec = None
+    if not args.no_decode:
+        log("[bench] decode workload")
+        dstep = Step(wl.WORKLOADS["decode"], dev, fp8=True)
+        d_total, _, d_stage = time_steps(dstep, 200, 20)
+        dec = {"us_per_call": round(d_total / 200 * 1e3, 2),
+               "layout_us": round(float(d_stage[:, 0].mean()) * 1e3, 2),
+               "dispatch_us": round(float(d_stage[:, 1].mean()) * 1e3, 2),
+               "combine_us": round(float(d_stage[:, 2].mean()) * 1e3, 2),
+               "bytes": dstep.bytes, "note": "warm (inputs stay in the 256 MB Infinity Cache), back-to-back"}
+        del dstep
+
+    cb = None if args.no_cpu_baseline else cpu_baseline(step)
+
+    comb_bytes = bytes_combine(w)
+    achieved = comb_bytes / (comb_ms / 1e3) / 1e9
+    traffic = measured_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: T={w.num_tokens} tokens, hidden={w.hidden}, E={w.num_experts} "
+                               f"experts in {w.num_ranks} virtual ranks, top-{w.num_topk} group-limited routing, "
+                               f"FP8 E4M3 1x128-scaled dispatch, BF16 combine",
+                   "tokens": w.num_tokens, "hidden": w.hidden, "experts": w.num_experts,
+                   "ranks": w.num_ranks, "topk": w.num_topk, "dispatch": "fp8_e4m3", "combine": "bf16",
+                   "bytes_per_step": step.bytes},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "stages_us": {"layout": round(float(lay_ms) * 1e3, 2), "dispatch": round(float(disp_ms) * 1e3, 2),
+                      "combine": round(float(comb_ms) * 1e3, 2)},
+        "stage_GBps": {"dispatch": round(bytes_dispatch(w, True) / (disp_ms / 1e3) / 1e9, 1),
+                       "combine": round(achieved, 1)},
+        "roofline": {"kernel": "combine", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": comb_bytes},
+        "decode": dec,
+        "cpu_baseline": cb,
+        "wall_s_timed": round(wall, 4),
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+// C ABI of the gfx950 MoE dispatch / combine library (declared in
+// include/ep.h): host-side argument checks, sizing, and kernel launches.
+// Every check runs before anything is enqueued.
+#include "ep.h"
+
+#include <hip/hip_runtime.h>
+
+#include "ep_internal.hpp"
+
+#define EP_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxRows = (int64_t)1 << 31;  // slots and pair ids are int32
+constexpr int kMaxHidden = 1 << 24;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+ep_status_t check_shape(const ep_shape_t* s) {
+  if (!s) return EP_ERR_INVALID_ARG;
+  if (s->num_tokens < 0 || s->hidden <= 0 || s->num_topk <= 0 || s->num_experts <= 0 || s->num_ranks <= 0)
+    return EP_ERR_INVALID_ARG;
+  if (s->num_experts % s->num_ranks != 0 || s->num_topk > s->num_experts) return EP_ERR_INVALID_ARG;
+  if (s->expert_alignment < 1 || s->capacity < 0) return EP_ERR_INVALID_ARG;
+  if (s->expert_alignment > 1 && s->capacity > 0) return EP_ERR_INVALID_ARG;
+  if (s->num_experts > EP_MAX_EXPERTS || s->num_topk > EP_MAX_TOPK) return EP_ERR_UNSUPPORTED;
+  if (s->hidden % 8 != 0 || s->hidden > kMaxHidden) return EP_ERR_UNSUPPORTED;
+  const int64_t T = s->num_tokens, k = s->num_topk, E = s->num_experts;
+  if (T * k >= kMaxRows) return EP_ERR_UNSUPPORTED;
+  const int64_t rows = s->capacity > 0 ? E * s->capacity : T * k + E * (s->expert_alignment - 1);
+  if (rows >= kMaxRows) return EP_ERR_UNSUPPORTED;
+  return EP_OK;
+}
+
+int64_t recv_rows_of(const ep_shape_t* s) {
+  const int64_t T = s->num_tokens, k = s->num_topk, E = s->num_experts;
+  return s->capacity > 0 ? E * s->capacity : T * k + E * (s->expert_alignment - 1);
+}
+
+ep_status_t hip_status(hipError_t err) {
+  if (err == hipSuccess) return EP_OK;
+  g_last_hip_error = (int)err;
+  return EP_ERR_HIP;
+}
+
+}  // namespace
+
+EP_EXPORT int ep_abi_version(void) { return EP_ABI_VERSION; }
+
+EP_EXPORT int ep_last_hip_error(void) { return g_last_hip_error; }
+
+EP_EXPORT const char* ep_status_string(ep_status_t status) {
+  switch (status) {
+    case EP_OK: return "EP_OK";
+    case EP_ERR_INVALID_ARG: return "EP_ERR_INVALID_ARG: null pointer or inconsistent shape";
+    case EP_ERR_UNSUPPORTED: return "EP_ERR_UNSUPPORTED: shape outside the supported limits";
+    case EP_ERR_MISALIGNED: return "EP_ERR_MISALIGNED: a row pointer is not 16-byte aligned";
+    case EP_ERR_WORKSPACE: return "EP_ERR_WORKSPACE: layout workspace missing or too small";
+    case EP_ERR_HIP: return "EP_ERR_HIP: a HIP launch failed (see ep_last_hip_error)";
+  }
+  return "unknown ep_status_t";
+}
+
+EP_EXPORT ep_status_t ep_recv_rows(const ep_shape_t* shape, int64_t* rows) {
+  const ep_status_t st = check_shape(shape);
+  if (st != EP_OK) return st;
+  if (!rows) return EP_ERR_INVALID_ARG;
+  *rows = recv_rows_of(shape);
+  return EP_OK;
+}
+
+EP_EXPORT ep_status_t ep_layout_workspace_bytes(const ep_shape_t* shape, size_t* bytes) {
+  const ep_status_t st = check_shape(shape);
+  if (st != EP_OK) return st;
+  if (!bytes) return EP_ERR_INVALID_ARG;
+  *bytes = ep::plan_layout(shape->num_tokens, shape->num_topk, shape->num_experts, shape->num_ranks).ws_bytes;
+  return EP_OK;
+}
+
+EP_EXPORT ep_status_t ep_layout(const ep_shape_t* shape, const int32_t* topk_idx, int32_t* expert_count,
+                                int32_t* expert_offset, int32_t* rank_count, int32_t* rank_offset, int32_t* slot,
+                                int32_t* src_pair, int32_t* diag, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  const ep_status_t st = check_shape(shape);
+  if (st != EP_OK) return st;
+  const int T = shape->num_tokens;
+  if (!expert_count || !expert_offset || !rank_count || !rank_offset) return EP_ERR_INVALID_ARG;
+  if (T > 0 && (!topk_idx || !slot)) return EP_ERR_INVALID_ARG;
+  const int32_t* ptrs[] = {topk_idx, expert_count, expert_offset, rank_count, rank_offset, slot, src_pair, diag};
+  for (const int32_t* q : ptrs)
+    if (!aligned(q, 4)) return EP_ERR_MISALIGNED;
+  const ep::LayoutPlan pl = ep::plan_layout(T, shape->num_topk, shape->num_experts, shape->num_ranks);
+  if (!workspace || workspace_bytes < pl.ws_bytes) return EP_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return EP_ERR_MISALIGNED;
+
+  ep::LayoutParams p{};
+  char* ws = static_cast<char*>(workspace);
+  p.idx = topk_idx;
+  p.expert_count = expert_count;
+  p.expert_offset = expert_offset;
+  p.rank_count = rank_count;
+  p.rank_offset = rank_offset;
+  p.slot = slot;
+  p.src_pair = src_pair;
+  p.diag = diag;
+  p.ticket = reinterpret_cast<uint32_t*>(ws);
+  p.ws_tile = reinterpret_cast<int32_t*>(ws + pl.ws_tile_off);
+  p.ws_rank = reinterpret_cast<int32_t*>(ws + pl.ws_rank_off);
+  p.ws_bad = reinterpret_cast<int32_t*>(ws + pl.ws_bad_off);
+  p.T = T;
+  p.k = shape->num_topk;
+  p.E = shape->num_experts;
+  p.R = shape->num_ranks;
+  p.A = shape->expert_alignment;
+  p.C = shape->capacity;
+  p.rows = recv_rows_of(shape);
+  return hip_status(ep::launch_layout(pl, p, stream));
+}
+
+EP_EXPORT ep_status_t ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t* slot,
+                                  ep_dtype_t recv_dtype, void* recv_x, float* recv_scale, hipStream_t stream) {
+  const ep_status_t st = check_shape(shape);
+  if (st != EP_OK) return st;
+  if (recv_dtype != EP_BF16 && recv_dtype != EP_FP8_E4M3) return EP_ERR_INVALID_ARG;
+  if (recv_dtype == EP_FP8_E4M3 && shape->hidden % 128 != 0) return EP_ERR_UNSUPPORTED;
+  const int T = shape->num_tokens;
+  if (T == 0) return EP_OK;
+  if (!x || !slot || !recv_x) return EP_ERR_INVALID_ARG;
+  if (recv_dtype == EP_FP8_E4M3 && !recv_scale) return EP_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(slot, 4) || !aligned(recv_scale, 4))
+    return EP_ERR_MISALIGNED;
+  ep::RowParams p{};
+  p.src = x;
+  p.slot = slot;
+  p.dst = recv_x;
+  p.recv_scale = recv_scale;
+  p.T = T;
+  p.H = shape->hidden;
+  p.k = shape->num_topk;
+  p.rows = recv_rows_of(shape);
+  return hip_status(recv_dtype == EP_BF16 ? ep::launch_dispatch_bf16(p, stream)
+                                          : ep::launch_dispatch_fp8(p, stream));
+}
+
+EP_EXPORT ep_status_t ep_combine(const ep_shape_t* shape, const void* y, const int32_t* slot,
+                                 const float* topk_weights, void* out, hipStream_t stream) {
+  const ep_status_t st = check_shape(shape);
+  if (st != EP_OK) return st;
+  const int T = shape->num_tokens;
+  if (T == 0) return EP_OK;
+  if (!y || !slot || !topk_weights || !out) return EP_ERR_INVALID_ARG;
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(slot, 4) || !aligned(topk_weights, 4))
+    return EP_ERR_MISALIGNED;
+  ep::RowParams p{};
+  p.src = y;
+  p.slot = slot;
+  p.weights = topk_weights;
+  p.dst = out;
+  p.T = T;
+  p.H = shape->hidden;
+  p.k = shape->num_topk;
+  p.rows = recv_rows_of(shape);
+  return hip_status(ep::launch_combine(p, stream));
+}
+
+EP_EXPORT ep_status_t ep_check_cvt_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
+  if (n < 0) return EP_ERR_INVALID_ARG;
+  if (n > 0 && (!in || !out)) return EP_ERR_INVALID_ARG;
+  if (!aligned(in, 4)) return EP_ERR_MISALIGNED;
+  return hip_status(ep::launch_check_cvt_e4m3(in, out, n, stream));
+}
+
+EP_EXPORT ep_status_t ep_check_cvt_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream) {
+  if (n < 0) return EP_ERR_INVALID_ARG;
+  if (n > 0 && (!in || !out)) return EP_ERR_INVALID_ARG;
+  if (!aligned(in, 4) || !aligned(out, 2)) return EP_ERR_MISALIGNED;
+  return hip_status(ep::launch_check_cvt_bf16(in, out, n, stream));
+}

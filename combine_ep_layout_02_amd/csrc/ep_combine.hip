@@ -1,0 +1,131 @@
+// Combine for gfx950: gather each token's k expert-output rows and write the
+// gate-weighted fp32 sum as BF16.
+//
+// Combine reduces the expert outputs back to the tokens' origin (DeepEP
+// documentation item 10; GeekNews "DeepSeek publica DeepEP ...", section
+// "Patrones de uso en entrenamiento, prefill y decoding"); here the origin
+// rows are local.  The sum is a fixed chain: acc = +0, then for j = 0..k-1
+// over valid slots acc = fmaf(w[t,j], y[slot[t,j], h], acc), then one BF16
+// round to nearest even (v_cvt_pk_bf16_f32).  A fixed order keeps the result
+// deterministic and equal to a scalar evaluation of the same chain.
+//
+// Work unit: one wavefront per (token, 1024-column chunk), as in dispatch.
+// All k row loads (2 x 16 bytes per lane each) are issued before the first
+// FMA, so a wavefront keeps 2k independent 1 KiB reads in flight.  Slots
+// and weights arrive with one vector load (lane j holds pair j) and are made
+// wave-uniform with v_readlane; an invalid slot gets an empty buffer range,
+// so its loads return zeros without touching memory and the FMA is skipped.
+#include "ep_device.hpp"
+#include "ep_internal.hpp"
+
+namespace ep {
+namespace {
+
+constexpr int kChunk = 1024;
+constexpr int kWavesPerBlock = 4;
+
+__device__ __forceinline__ void fma8(float* acc, float w, u32x4 v) {
+  acc[0] = __builtin_fmaf(w, bf16_lo(v.x), acc[0]);
+  acc[1] = __builtin_fmaf(w, bf16_hi(v.x), acc[1]);
+  acc[2] = __builtin_fmaf(w, bf16_lo(v.y), acc[2]);
+  acc[3] = __builtin_fmaf(w, bf16_hi(v.y), acc[3]);
+  acc[4] = __builtin_fmaf(w, bf16_lo(v.z), acc[4]);
+  acc[5] = __builtin_fmaf(w, bf16_hi(v.z), acc[5]);
+  acc[6] = __builtin_fmaf(w, bf16_lo(v.w), acc[6]);
+  acc[7] = __builtin_fmaf(w, bf16_hi(v.w), acc[7]);
+}
+
+__device__ __forceinline__ u32x4 pack8(const float* acc) {
+  u32x4 o;
+  o.x = pack_bf16x2(acc[0], acc[1]);
+  o.y = pack_bf16x2(acc[2], acc[3]);
+  o.z = pack_bf16x2(acc[4], acc[5]);
+  o.w = pack_bf16x2(acc[6], acc[7]);
+  return o;
+}
+
+// Rows j0 .. j0+NB-1 of the chain (NB known at compile time; rows >= k are
+// empty).  Loads first, then the FMAs in j order.
+template <int NB, int AUX_LD>
+__device__ __forceinline__ void accumulate(const uint16_t* y, int64_t rows, int H, int k, int j0, int sl,
+                                           int wl, uint32_t colA, uint32_t colB, float* accA, float* accB) {
+  u32x4 ya[NB], yb[NB];
+  bool ok[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int j = j0 + i;
+    const int s = __builtin_amdgcn_readlane(sl, j & 63);
+    ok[i] = j < k && s >= 0 && (int64_t)s < rows;
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(y + (ok[i] ? (int64_t)s * H : 0), ok[i] ? (uint32_t)H * 2u : 0u);
+    ya[i] = load16<AUX_LD>(r, colA * 2u);
+    yb[i] = load16<AUX_LD>(r, colB * 2u);
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    if (!ok[i]) continue;
+    const float w = __uint_as_float((uint32_t)__builtin_amdgcn_readlane(wl, (j0 + i) & 63));
+    fma8(accA, w, ya[i]);
+    fma8(accB, w, yb[i]);
+  }
+}
+
+template <int K, int AUX_LD, int AUX_ST>
+__global__ __launch_bounds__(256) void combine_kernel(RowParams p, int chunks) {
+  const int lane = threadIdx.x & 63;
+  const int item = uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const int t = item / chunks;
+  if (t >= p.T) return;
+  const int c = item - t * chunks;
+  const int H = p.H;
+  const int k = K > 0 ? K : p.k;
+  const uint32_t colA = (uint32_t)(c * kChunk + lane * 8), colB = colA + 512;
+
+  int sl = -1, wl = 0;
+  if (lane < k) {
+    sl = p.slot[(int64_t)t * k + lane];
+    wl = (int)__float_as_uint(p.weights[(int64_t)t * k + lane]);
+  }
+  const uint16_t* y = static_cast<const uint16_t*>(p.src);
+  float accA[8], accB[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { accA[i] = 0.0f; accB[i] = 0.0f; }
+
+  if constexpr (K > 0) {
+    accumulate<K, AUX_LD>(y, p.rows, H, k, 0, sl, wl, colA, colB, accA, accB);
+  } else {
+    for (int j0 = 0; j0 < k; j0 += 8)
+      accumulate<8, AUX_LD>(y, p.rows, H, k, j0, sl, wl, colA, colB, accA, accB);
+  }
+
+  uint16_t* out = static_cast<uint16_t*>(p.dst) + (int64_t)t * H;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, (uint32_t)H * 2u);
+  store16<AUX_ST>(ro, colA * 2u, pack8(accA));
+  store16<AUX_ST>(ro, colB * 2u, pack8(accB));
+}
+
+template <int K>
+hipError_t launch_k(const RowParams& p, int blocks, int chunks, hipStream_t stream) {
+  hipLaunchKernelGGL((combine_kernel<K, kAuxDefault, kAuxDefault>), dim3(blocks), dim3(256), 0, stream, p,
+                     chunks);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(const RowParams& p, hipStream_t stream) {
+  if (p.T == 0) return hipSuccess;
+  const int chunks = (p.H + kChunk - 1) / kChunk;
+  const int64_t items = (int64_t)p.T * chunks;
+  const int blocks = (int)((items + kWavesPerBlock - 1) / kWavesPerBlock);
+  switch (p.k) {
+    case 1: return launch_k<1>(p, blocks, chunks, stream);
+    case 2: return launch_k<2>(p, blocks, chunks, stream);
+    case 4: return launch_k<4>(p, blocks, chunks, stream);
+    case 6: return launch_k<6>(p, blocks, chunks, stream);
+    case 8: return launch_k<8>(p, blocks, chunks, stream);
+    default: return launch_k<0>(p, blocks, chunks, stream);
+  }
+}
+
+}  // namespace ep

@@ -1,0 +1,56 @@
+// Internal interfaces between the C ABI (ep_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ep {
+
+struct LayoutParams {
+  const int32_t* idx;
+  int32_t* expert_count;
+  int32_t* expert_offset;
+  int32_t* rank_count;
+  int32_t* rank_offset;
+  int32_t* slot;
+  int32_t* src_pair;  // may be null
+  int32_t* diag;      // may be null
+  int32_t* ws_tile;   // [ntiles][E] tile counts, then tile bases
+  int32_t* ws_rank;   // [ntiles][R] distinct tokens per rank and tile
+  int32_t* ws_bad;    // [ntiles] invalid ids per tile
+  uint32_t* ticket;   // tile-completion counter, zero between calls
+  int T, k, E, R, A, C;
+  int W;       // 64-pair windows (wavefronts) per tile
+  int TT;      // tokens per tile
+  int ntiles;
+  int64_t rows;  // worst-case receive rows (length of src_pair)
+};
+
+struct LayoutPlan {
+  int W, TT, ntiles, threads;
+  size_t lds_bytes;
+  size_t ws_tile_off, ws_rank_off, ws_bad_off, ws_bytes;
+};
+
+LayoutPlan plan_layout(int T, int k, int E, int R);
+hipError_t launch_layout(const LayoutPlan& plan, LayoutParams p, hipStream_t stream);
+
+struct RowParams {
+  const void* src;          // x (dispatch) or y (combine)
+  const int32_t* slot;
+  const float* weights;     // combine only
+  void* dst;                // recv_x (dispatch) or out (combine)
+  float* recv_scale;        // FP8 dispatch only
+  int T, H, k;
+  int64_t rows;             // receive rows (bounds for slot values)
+};
+
+hipError_t launch_dispatch_bf16(const RowParams& p, hipStream_t stream);
+hipError_t launch_dispatch_fp8(const RowParams& p, hipStream_t stream);
+hipError_t launch_combine(const RowParams& p, hipStream_t stream);
+
+hipError_t launch_check_cvt_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
+hipError_t launch_check_cvt_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream);
+
+}  // namespace ep

@@ -1,0 +1,260 @@
+"""Python binding of libep.so (C ABI in include/ep.h), argument marshalling only.
+
+The functions carry the C names and take torch tensors for device buffers:
+each call checks dtype, device, contiguity and size, passes raw pointers and
+the current HIP stream, and raises :class:`EpError` on a non-zero status.
+Every step of the path runs in the library's HIP kernels; PyTorch only
+provides the device memory and the stream.  If libep.so has not been built
+the first call raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libep.so")
+_lib = None
+
+EP_BF16 = 0
+EP_FP8_E4M3 = 1
+EP_OK = 0
+EP_MAX_EXPERTS = 2048
+EP_MAX_TOPK = 64
+
+EXPORTED = ("ep_recv_rows", "ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_combine",
+            "ep_status_string", "ep_abi_version", "ep_last_hip_error", "ep_check_cvt_e4m3",
+            "ep_check_cvt_bf16")
+
+
+class EpError(RuntimeError):
+    def __init__(self, func: str, status: int, hip_error: int = 0):
+        msg = f"{func} failed: {status_string(status)}"
+        if hip_error:
+            msg += f" (hipError {hip_error})"
+        super().__init__(msg)
+        self.status = status
+        self.hip_error = hip_error
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("num_tokens", "hidden", "num_topk", "num_experts",
+                                                "num_ranks", "expert_alignment", "capacity")]
+
+
+@dataclass(frozen=True)
+class EpShape:
+    """ep_shape_t: T tokens of hidden H routed to k of E experts in R ranks."""
+    num_tokens: int
+    hidden: int
+    num_topk: int
+    num_experts: int
+    num_ranks: int
+    expert_alignment: int = 1
+    capacity: int = 0
+
+    def c(self) -> _Shape:
+        return _Shape(self.num_tokens, self.hidden, self.num_topk, self.num_experts, self.num_ranks,
+                      self.expert_alignment, self.capacity)
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libep.so; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m combine_ep_layout_02_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, sp = ctypes.c_void_p, ctypes.POINTER(_Shape)
+        st = ctypes.c_int
+        L.ep_abi_version.restype = ctypes.c_int
+        L.ep_last_hip_error.restype = ctypes.c_int
+        L.ep_status_string.restype = ctypes.c_char_p
+        L.ep_status_string.argtypes = [st]
+        L.ep_recv_rows.restype = st
+        L.ep_recv_rows.argtypes = [sp, ctypes.POINTER(ctypes.c_int64)]
+        L.ep_layout_workspace_bytes.restype = st
+        L.ep_layout_workspace_bytes.argtypes = [sp, ctypes.POINTER(ctypes.c_size_t)]
+        L.ep_layout.restype = st
+        L.ep_layout.argtypes = [sp] + [vp] * 9 + [ctypes.c_size_t, vp]
+        L.ep_dispatch.restype = st
+        L.ep_dispatch.argtypes = [sp, vp, vp, ctypes.c_int, vp, vp, vp]
+        L.ep_combine.restype = st
+        L.ep_combine.argtypes = [sp, vp, vp, vp, vp, vp]
+        L.ep_check_cvt_e4m3.restype = st
+        L.ep_check_cvt_e4m3.argtypes = [vp, vp, ctypes.c_int64, vp]
+        L.ep_check_cvt_bf16.restype = st
+        L.ep_check_cvt_bf16.argtypes = [vp, vp, ctypes.c_int64, vp]
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().ep_status_string(int(status)).decode()
+
+
+def ep_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def ep_abi_version() -> int:
+    return int(lib().ep_abi_version())
+
+
+def _check(func: str, status: int) -> None:
+    if status != EP_OK:
+        raise EpError(func, status, int(lib().ep_last_hip_error()) if status == 5 else 0)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, numel: Optional[int] = None,
+         optional: bool = False) -> Optional[int]:
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    if t.numel() and t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device (cuda/HIP) tensor")
+    return t.data_ptr() if t.numel() else None
+
+
+_BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
+_BYTE_LIKE = (torch.uint8, torch.float8_e4m3fn, torch.int8)
+
+
+def ep_recv_rows(shape: EpShape) -> int:
+    out = ctypes.c_int64()
+    _check("ep_recv_rows", lib().ep_recv_rows(ctypes.byref(shape.c()), ctypes.byref(out)))
+    return out.value
+
+
+def ep_layout_workspace_bytes(shape: EpShape) -> int:
+    out = ctypes.c_size_t()
+    _check("ep_layout_workspace_bytes", lib().ep_layout_workspace_bytes(ctypes.byref(shape.c()), ctypes.byref(out)))
+    return out.value
+
+
+def ep_layout(shape: EpShape, topk_idx, expert_count, expert_offset, rank_count, rank_offset, slot,
+              src_pair=None, diag=None, workspace=None, stream=None) -> None:
+    T, k, E, R = shape.num_tokens, shape.num_topk, shape.num_experts, shape.num_ranks
+    rows = ep_recv_rows(shape)
+    ws_bytes = ep_layout_workspace_bytes(shape)
+    i32 = torch.int32
+    args = (
+        _ptr(topk_idx, "topk_idx", i32, T * k, optional=T == 0),
+        _ptr(expert_count, "expert_count", i32, E), _ptr(expert_offset, "expert_offset", i32, E + 1),
+        _ptr(rank_count, "rank_count", i32, R), _ptr(rank_offset, "rank_offset", i32, R + 1),
+        _ptr(slot, "slot", i32, T * k, optional=T == 0),
+        _ptr(src_pair, "src_pair", i32, rows, optional=True), _ptr(diag, "diag", i32, 2, optional=True),
+        _ptr(workspace, "workspace", None, None),
+    )
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < ws_bytes:
+        raise ValueError(f"workspace has {nbytes} bytes, needs {ws_bytes}")
+    _check("ep_layout", lib().ep_layout(ctypes.byref(shape.c()), *args, nbytes, _stream(stream)))
+
+
+def ep_dispatch(shape: EpShape, x, slot, recv_dtype: int, recv_x, recv_scale=None, stream=None) -> None:
+    T, H, k = shape.num_tokens, shape.hidden, shape.num_topk
+    rows = ep_recv_rows(shape)
+    if recv_dtype == EP_BF16:
+        rx = _ptr(recv_x, "recv_x", _BF16_LIKE, rows * H)
+        rs = None
+    elif recv_dtype == EP_FP8_E4M3:
+        rx = _ptr(recv_x, "recv_x", _BYTE_LIKE, rows * H)
+        rs = _ptr(recv_scale, "recv_scale", torch.float32, rows * (H // 128))
+    else:
+        raise ValueError(f"unknown recv_dtype {recv_dtype}")
+    _check("ep_dispatch", lib().ep_dispatch(
+        ctypes.byref(shape.c()), _ptr(x, "x", _BF16_LIKE, T * H, optional=T == 0),
+        _ptr(slot, "slot", torch.int32, T * k, optional=T == 0), int(recv_dtype), rx, rs, _stream(stream)))
+
+
+def ep_combine(shape: EpShape, y, slot, topk_weights, out, stream=None) -> None:
+    T, H, k = shape.num_tokens, shape.hidden, shape.num_topk
+    rows = ep_recv_rows(shape)
+    _check("ep_combine", lib().ep_combine(
+        ctypes.byref(shape.c()), _ptr(y, "y", _BF16_LIKE, rows * H, optional=T == 0),
+        _ptr(slot, "slot", torch.int32, T * k, optional=T == 0),
+        _ptr(topk_weights, "topk_weights", torch.float32, T * k, optional=T == 0),
+        _ptr(out, "out", _BF16_LIKE, T * H, optional=T == 0), _stream(stream)))
+
+
+def ep_check_cvt_e4m3(inp, out, stream=None) -> None:
+    n = inp.numel()
+    _check("ep_check_cvt_e4m3", lib().ep_check_cvt_e4m3(
+        _ptr(inp, "in", torch.float32, n, optional=n == 0), _ptr(out, "out", _BYTE_LIKE, n, optional=n == 0),
+        n, _stream(stream)))
+
+
+def ep_check_cvt_bf16(inp, out, stream=None) -> None:
+    n = inp.numel()
+    _check("ep_check_cvt_bf16", lib().ep_check_cvt_bf16(
+        _ptr(inp, "in", torch.float32, n, optional=n == 0), _ptr(out, "out", _BF16_LIKE, n, optional=n == 0),
+        n, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Convenience: allocate outputs with torch, then call the entry points above.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class LayoutBuffers:
+    """The routing handle: ep_layout outputs (plus its workspace)."""
+    shape: EpShape
+    expert_count: torch.Tensor
+    expert_offset: torch.Tensor
+    rank_count: torch.Tensor
+    rank_offset: torch.Tensor
+    slot: torch.Tensor
+    src_pair: torch.Tensor
+    diag: torch.Tensor
+    workspace: torch.Tensor
+
+    @staticmethod
+    def allocate(shape: EpShape, device="cuda") -> "LayoutBuffers":
+        i32 = dict(dtype=torch.int32, device=device)
+        E, R = shape.num_experts, shape.num_ranks
+        ws = ep_layout_workspace_bytes(shape)
+        return LayoutBuffers(
+            shape, torch.empty(E, **i32), torch.empty(E + 1, **i32), torch.empty(R, **i32),
+            torch.empty(R + 1, **i32), torch.empty((shape.num_tokens, shape.num_topk), **i32),
+            torch.empty(ep_recv_rows(shape), **i32), torch.empty(2, **i32),
+            # zero-filled once; ep_layout leaves it zeroed after every call
+            torch.zeros((ws + 15) // 16 * 4, **i32))
+
+    def run(self, topk_idx: torch.Tensor, stream=None) -> "LayoutBuffers":
+        ep_layout(self.shape, topk_idx, self.expert_count, self.expert_offset, self.rank_count,
+                  self.rank_offset, self.slot, self.src_pair, self.diag, self.workspace, stream)
+        return self
+
+
+def alloc_recv(shape: EpShape, recv_dtype: int, device="cuda"):
+    rows, H = ep_recv_rows(shape), shape.hidden
+    if recv_dtype == EP_BF16:
+        return torch.empty((rows, H), dtype=torch.bfloat16, device=device), None
+    return (torch.empty((rows, H), dtype=torch.uint8, device=device),
+            torch.empty((rows, H // 128), dtype=torch.float32, device=device))

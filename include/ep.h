@@ -1,0 +1,212 @@
+/*
+ * ep.h - C ABI of the MI355X (gfx950) MoE dispatch / combine library.
+ *
+ * One GPU's share of DeepEP-style expert-parallel dispatch and combine,
+ * without the inter-GPU exchange.  The "ranks" here are segments of one
+ * expert-major receive buffer in HBM.  Three stages:
+ *
+ *   ep_layout    top-k expert ids -> per-expert / per-rank counts, prefix
+ *                offsets and the token->slot map (the routing handle).
+ *   ep_dispatch  scatter BF16 tokens into the receive buffer, as BF16 or as
+ *                FP8 E4M3 with one fp32 scale per 128 columns.
+ *   ep_combine   gather expert outputs back to token order as the gate-
+ *                weighted fp32 sum of the top-k rows, written as BF16.
+ *
+ * Sources for what the operations are (the pages print no code):
+ *   [GN]  GeekNews "DeepSeek publica DeepEP, una biblioteca open source para
+ *         entrenamiento e inferencia MoE" (es.news.hada.io), sections
+ *         "Resultados de medición de rendimiento", "Interfaz centrada en
+ *         ElasticBuffer", "Patrones de uso en entrenamiento, prefill y
+ *         decoding".
+ *   [DOC] "DeepEP (DeepEveryParallel) Documentation" (docsearch.algolia.com),
+ *         items 3 ("... for Inference Decoding") and 10 ("... for Training
+ *         or Prefilling").
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers (hipMalloc / torch CUDA
+ *     tensors), row-major and contiguous; `shape` is a HOST pointer.
+ *   - The caller owns every buffer, including the layout workspace.  The
+ *     library allocates nothing, keeps no state between calls and may be
+ *     called from several host threads at once.
+ *   - Work is only enqueued on `stream` (0 = the null stream); nothing
+ *     synchronises the host.  Results are valid in stream order.
+ *   - Arguments are checked on the host before anything is enqueued; on any
+ *     error nothing is launched and the status says why.
+ *   - Bad data on the device (an expert id outside [-1, E), a pair beyond
+ *     a padded expert's capacity) is never fatal: such pairs get slot -1
+ *     and are counted in diag.
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EP_ABI_VERSION 1
+
+/* Limits checked by every entry point (EP_ERR_UNSUPPORTED beyond them). */
+#define EP_MAX_EXPERTS 2048
+#define EP_MAX_TOPK 64
+
+/*
+ * Problem shape.  T tokens of hidden size H, each routed to k experts out of
+ * E; the E experts are split into R contiguous groups of E/R ("ranks").
+ * The arguments mirror DeepEP's buffer and dispatch parameters (maximum
+ * tokens, hidden, num_topk, num_experts, expert_alignment: [GN] "Interfaz
+ * centrada en ElasticBuffer"; [DOC] item 10).
+ *
+ *   num_tokens        T >= 0
+ *   hidden            H > 0, a multiple of 8 (of 128 for FP8 dispatch)
+ *   num_topk          k in [1, EP_MAX_TOPK], k <= E
+ *   num_experts       E in [1, EP_MAX_EXPERTS]
+ *   num_ranks         R >= 1, R divides E
+ *   expert_alignment  A >= 1: each expert's segment of the flat layout is
+ *                     padded to a multiple of A rows (for grouped GEMMs)
+ *   capacity          C >= 0: 0 = flat expert-major layout; C > 0 = padded
+ *                     per-expert layout [E, C] (low-latency decode form),
+ *                     requires A == 1
+ */
+typedef struct ep_shape_t {
+    int32_t num_tokens;
+    int32_t hidden;
+    int32_t num_topk;
+    int32_t num_experts;
+    int32_t num_ranks;
+    int32_t expert_alignment;
+    int32_t capacity;
+} ep_shape_t;
+
+typedef enum ep_dtype_t {
+    EP_BF16 = 0,      /* receive rows are BF16 copies of the tokens        */
+    EP_FP8_E4M3 = 1   /* receive rows are OCP E4M3FN codes + fp32 scales    */
+} ep_dtype_t;
+
+typedef enum ep_status_t {
+    EP_OK = 0,
+    EP_ERR_INVALID_ARG = 1,  /* null pointer or inconsistent shape           */
+    EP_ERR_UNSUPPORTED = 2,  /* shape outside the supported limits           */
+    EP_ERR_MISALIGNED = 3,   /* a row pointer is not 16-byte aligned         */
+    EP_ERR_WORKSPACE = 4,    /* workspace missing or too small               */
+    EP_ERR_HIP = 5           /* a HIP launch failed; see ep_last_hip_error() */
+} ep_status_t;
+
+/*
+ * Rows of the receive buffer (recv_x, recv_scale, y, src_pair) for `shape`:
+ * T*k + E*(A-1) for the flat layout, E*C for the padded one.  This is the
+ * worst case over all routings, so buffers of this size never overflow and
+ * no device->host count read is needed (the analog of sizing DeepEP's buffer
+ * from its maximum token count: [GN] "Interfaz centrada en ElasticBuffer").
+ * Host only.
+ */
+ep_status_t ep_recv_rows(const ep_shape_t *shape, int64_t *rows);
+
+/*
+ * Bytes of device workspace ep_layout needs for `shape`.  Host only.
+ * The workspace must be zero-filled once before its first use; every
+ * ep_layout call leaves it zeroed again for the next one.  One workspace
+ * must not be used by two ep_layout calls that may overlap in time.
+ */
+ep_status_t ep_layout_workspace_bytes(const ep_shape_t *shape, size_t *bytes);
+
+/*
+ * Routing layout: the per-expert counts the expert GEMM needs and the
+ * routing metadata combine needs ([GN] "Patrones de uso en entrenamiento,
+ * prefill y decoding"; [DOC] item 10).  The outputs are the reusable
+ * handle: calling ep_dispatch / ep_combine again with the same `slot` is
+ * the cached-handle path that skips the layout ([DOC] item 3).
+ *
+ *   topk_idx      int32 [T, k]  expert of pair (t, j); -1 = masked pair
+ *   expert_count  int32 [E]     pairs routed to each expert (true count,
+ *                               also when the padded layout drops pairs)
+ *   expert_offset int32 [E+1]   first receive row of each expert; [E] is
+ *                               the end of the flat layout (e*C if padded)
+ *   rank_count    int32 [R]     distinct tokens with >= 1 expert in rank r
+ *                               (rank r owns experts [r*E/R, (r+1)*E/R))
+ *   rank_offset   int32 [R+1]   expert_offset[r*E/R]
+ *   slot          int32 [T, k]  receive row of pair (t, j), or -1
+ *   src_pair      int32 [ep_recv_rows] or NULL: pair t*k+j held by each
+ *                               receive row, -1 for padding rows
+ *   diag          int32 [2] or NULL: [0] ids outside [-1, E), [1] pairs
+ *                               dropped by the padded layout's capacity
+ *   workspace     device buffer of ep_layout_workspace_bytes (see there)
+ *
+ * Slot order inside an expert is ascending (t, j): the layout is a stable
+ * counting sort of the pairs by expert, deterministic bit for bit.
+ */
+ep_status_t ep_layout(const ep_shape_t *shape, const int32_t *topk_idx,
+                      int32_t *expert_count, int32_t *expert_offset,
+                      int32_t *rank_count, int32_t *rank_offset,
+                      int32_t *slot, int32_t *src_pair, int32_t *diag,
+                      void *workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/*
+ * Dispatch: every pair (t, j) with slot >= 0 receives token t
+ * ([DOC] item 10: dispatch routes tokens to their experts, in BF16 or FP8).
+ *
+ *   x          BF16 [T, H]      tokens (bit patterns, 16-byte aligned)
+ *   slot       int32 [T, k]     from ep_layout
+ *   recv_dtype EP_BF16:     recv_x is BF16 [rows, H], a bit copy of x[t];
+ *              EP_FP8_E4M3: recv_x is uint8 [rows, H] OCP E4M3FN codes and
+ *                           recv_scale fp32 [rows, H/128]: per 128-column
+ *                           block b, s = max(amax_b, 1e-4) / 448 and
+ *                           code = E4M3_RNE_SAT(x / s), both in fp32, with
+ *                           a correctly rounded division
+ *   recv_x     [ep_recv_rows, H], 16-byte aligned; rows that no pair maps
+ *              to are left untouched
+ *   recv_scale fp32 [ep_recv_rows, H/128] for FP8, else ignored (may be NULL)
+ */
+ep_status_t ep_dispatch(const ep_shape_t *shape, const void *x, const int32_t *slot,
+                        ep_dtype_t recv_dtype, void *recv_x, float *recv_scale,
+                        hipStream_t stream);
+
+/*
+ * Combine: the expert outputs are reduced back to token order
+ * ([DOC] item 10; [GN] "Patrones de uso ..."):
+ *   out[t, h] = BF16_RNE( acc ),  acc = +0, then for j = 0..k-1 with
+ *               slot[t, j] >= 0:  acc = fmaf(w[t, j], y[slot[t, j], h], acc)
+ * The fixed order makes the result deterministic and identical to a scalar
+ * evaluation of the same chain.
+ *
+ *   y             BF16 [ep_recv_rows, H]   expert outputs in receive layout
+ *   slot          int32 [T, k]             from ep_layout
+ *   topk_weights  fp32 [T, k]              gate weights (no renormalisation)
+ *   out           BF16 [T, H]
+ */
+ep_status_t ep_combine(const ep_shape_t *shape, const void *y, const int32_t *slot,
+                       const float *topk_weights, void *out, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *ep_status_string(ep_status_t status);
+
+/* EP_ABI_VERSION of the loaded library. */
+int ep_abi_version(void);
+
+/* hipError_t of the last EP_ERR_HIP returned on the calling thread, else 0. */
+int ep_last_hip_error(void);
+
+/*
+ * Conversion check helpers.  They run, element by element, the exact device
+ * routines ep_dispatch and ep_combine use for their final rounding steps, so
+ * a test can sweep whole input ranges:
+ *   ep_check_cvt_e4m3: out[i] = E4M3 code of in[i], round to nearest even;
+ *                      defined for |in[i]| <= 464 (E4M3FN's top code 448 and
+ *                      its rounding half-step), which covers every quotient
+ *                      FP8 dispatch produces (|x / s| <= 448 plus one ulp)
+ *   ep_check_cvt_bf16: out[i] = BF16_RNE(in[i]) for finite in[i]
+ * in is a device fp32 array of n elements, out a device array of n codes
+ * (uint8) or BF16 bit patterns (uint16); n >= 0.
+ */
+ep_status_t ep_check_cvt_e4m3(const float *in, uint8_t *out, int64_t n, hipStream_t stream);
+ep_status_t ep_check_cvt_bf16(const float *in, uint16_t *out, int64_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_H */

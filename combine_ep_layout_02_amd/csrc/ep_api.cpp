@@ -105,7 +105,6 @@ EP_EXPORT ep_status_t ep_layout(const ep_shape_t* shape, const int32_t* topk_idx
   p.slot = slot;
   p.src_pair = src_pair;
   p.diag = diag;
-  p.ticket = reinterpret_cast<uint32_t*>(ws);
   p.ws_tile = reinterpret_cast<int32_t*>(ws + pl.ws_tile_off);
   p.ws_rank = reinterpret_cast<int32_t*>(ws + pl.ws_rank_off);
   p.ws_bad = reinterpret_cast<int32_t*>(ws + pl.ws_bad_off);

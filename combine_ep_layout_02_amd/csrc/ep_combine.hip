@@ -9,9 +9,9 @@
 // round to nearest even (v_cvt_pk_bf16_f32).  A fixed order keeps the result
 // deterministic and equal to a scalar evaluation of the same chain.
 //
-// Work unit: one wavefront per (token, 1024-column chunk), as in dispatch.
-// All k row loads (2 x 16 bytes per lane each) are issued before the first
-// FMA, so a wavefront keeps 2k independent 1 KiB reads in flight.  Slots
+// Work unit: one wavefront per (token, column chunk).  All k row loads
+// (16 bytes per lane and column group each) are issued before the first FMA,
+// so a wavefront keeps k * groups independent 1 KiB reads in flight.  Slots
 // and weights arrive with one vector load (lane j holds pair j) and are made
 // wave-uniform with v_readlane; an invalid slot gets an empty buffer range,
 // so its loads return zeros without touching memory and the FMA is skipped.
@@ -21,7 +21,14 @@
 namespace ep {
 namespace {
 
-constexpr int kChunk = 1024;
+// 16-byte column groups per lane per row: the work unit covers 512 * groups
+// columns.
+#ifndef EP_COMBINE_GROUPS
+#define EP_COMBINE_GROUPS 2
+#endif
+
+constexpr int kGroups = EP_COMBINE_GROUPS;
+constexpr int kChunk = 512 * kGroups;
 constexpr int kWavesPerBlock = 4;
 
 __device__ __forceinline__ void fma8(float* acc, float w, u32x4 v) {
@@ -45,11 +52,11 @@ __device__ __forceinline__ u32x4 pack8(const float* acc) {
 }
 
 // Rows j0 .. j0+NB-1 of the chain (NB known at compile time; rows >= k are
-// empty).  Loads first, then the FMAs in j order.
-template <int NB, int AUX_LD>
+// empty).  All loads first, then the FMAs in j order.
+template <int NB, int NG, int AUX_LD>
 __device__ __forceinline__ void accumulate(const uint16_t* y, int64_t rows, int H, int k, int j0, int sl,
-                                           int wl, uint32_t colA, uint32_t colB, float* accA, float* accB) {
-  u32x4 ya[NB], yb[NB];
+                                           int wl, uint32_t col0, float (&acc)[NG][8]) {
+  u32x4 v[NB][NG];
   bool ok[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
@@ -58,15 +65,15 @@ __device__ __forceinline__ void accumulate(const uint16_t* y, int64_t rows, int 
     ok[i] = j < k && s >= 0 && (int64_t)s < rows;
     const __amdgpu_buffer_rsrc_t r =
         make_rsrc(y + (ok[i] ? (int64_t)s * H : 0), ok[i] ? (uint32_t)H * 2u : 0u);
-    ya[i] = load16<AUX_LD>(r, colA * 2u);
-    yb[i] = load16<AUX_LD>(r, colB * 2u);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) v[i][g] = load16<AUX_LD>(r, (col0 + 512u * g) * 2u);
   }
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     if (!ok[i]) continue;
     const float w = __uint_as_float((uint32_t)__builtin_amdgcn_readlane(wl, (j0 + i) & 63));
-    fma8(accA, w, ya[i]);
-    fma8(accB, w, yb[i]);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) fma8(acc[g], w, v[i][g]);
   }
 }
 
@@ -79,7 +86,7 @@ __global__ __launch_bounds__(256) void combine_kernel(RowParams p, int chunks) {
   const int c = item - t * chunks;
   const int H = p.H;
   const int k = K > 0 ? K : p.k;
-  const uint32_t colA = (uint32_t)(c * kChunk + lane * 8), colB = colA + 512;
+  const uint32_t col0 = (uint32_t)(c * kChunk + lane * 8);
 
   int sl = -1, wl = 0;
   if (lane < k) {
@@ -87,27 +94,30 @@ __global__ __launch_bounds__(256) void combine_kernel(RowParams p, int chunks) {
     wl = (int)__float_as_uint(p.weights[(int64_t)t * k + lane]);
   }
   const uint16_t* y = static_cast<const uint16_t*>(p.src);
-  float accA[8], accB[8];
+  float acc[kGroups][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) { accA[i] = 0.0f; accB[i] = 0.0f; }
+  for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[g][i] = 0.0f;
 
   if constexpr (K > 0) {
-    accumulate<K, AUX_LD>(y, p.rows, H, k, 0, sl, wl, colA, colB, accA, accB);
+    accumulate<K, kGroups, AUX_LD>(y, p.rows, H, k, 0, sl, wl, col0, acc);
   } else {
-    for (int j0 = 0; j0 < k; j0 += 8)
-      accumulate<8, AUX_LD>(y, p.rows, H, k, j0, sl, wl, colA, colB, accA, accB);
+    for (int j0 = 0; j0 < k; j0 += 8) accumulate<8, kGroups, AUX_LD>(y, p.rows, H, k, j0, sl, wl, col0, acc);
   }
 
   uint16_t* out = static_cast<uint16_t*>(p.dst) + (int64_t)t * H;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, (uint32_t)H * 2u);
-  store16<AUX_ST>(ro, colA * 2u, pack8(accA));
-  store16<AUX_ST>(ro, colB * 2u, pack8(accB));
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) store16<AUX_ST>(ro, (col0 + 512u * g) * 2u, pack8(acc[g]));
 }
 
 template <int K>
 hipError_t launch_k(const RowParams& p, int blocks, int chunks, hipStream_t stream) {
-  hipLaunchKernelGGL((combine_kernel<K, kAuxDefault, kAuxDefault>), dim3(blocks), dim3(256), 0, stream, p,
-                     chunks);
+  if ((int64_t)p.T * p.k * p.H * 2 >= kStreamingBytes)
+    hipLaunchKernelGGL((combine_kernel<K, kAuxNT, kAuxNT>), dim3(blocks), dim3(256), 0, stream, p, chunks);
+  else
+    hipLaunchKernelGGL((combine_kernel<K, kAuxDefault, kAuxDefault>), dim3(blocks), dim3(256), 0, stream, p, chunks);
   return hipGetLastError();
 }
 

@@ -27,6 +27,12 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr int kAuxDefault = 0;
 constexpr int kAuxNT = 2;  // non-temporal: stream through, do not keep
 
+// Receive-buffer traffic above which dispatch / combine switch to
+// non-temporal row accesses.  Small (decode-sized) calls keep their rows in
+// L2 and the 256 MB Infinity Cache; large ones stream, so the written rows do
+// not sit dirty in the caches and the gathered rows do not evict them.
+constexpr int64_t kStreamingBytes = (int64_t)64 << 20;
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)num_bytes, kBufferWord3);
 }

@@ -16,20 +16,25 @@ struct LayoutParams {
   int32_t* slot;
   int32_t* src_pair;  // may be null
   int32_t* diag;      // may be null
-  int32_t* ws_tile;   // [ntiles][E] tile counts, then tile bases
-  int32_t* ws_rank;   // [ntiles][R] distinct tokens per rank and tile
+  int32_t* ws_tile;   // [ntiles][E] pairs per (tile, expert)
+  int32_t* ws_rank;   // [ntiles][R] distinct tokens per (tile, rank)
   int32_t* ws_bad;    // [ntiles] invalid ids per tile
-  uint32_t* ticket;   // tile-completion counter, zero between calls
   int T, k, E, R, A, C;
   int W;       // 64-pair windows (wavefronts) per tile
   int TT;      // tokens per tile
   int ntiles;
+  int G;       // tile groups per expert in the finalize kernel
+  // n / d == __umulhi(n, magic_d) for the n that occur (n * d < 2^32):
+  uint32_t magic_k;    // d = k
+  uint32_t magic_per;  // d = E / R
+  uint32_t magic_E;    // d = E
+  uint32_t magic_R;    // d = R
   int64_t rows;  // worst-case receive rows (length of src_pair)
 };
 
 struct LayoutPlan {
-  int W, TT, ntiles, threads;
-  size_t lds_bytes;
+  int W, TT, ntiles, threads, G, fin_threads;
+  size_t lds_bytes, fin_lds_bytes;
   size_t ws_tile_off, ws_rank_off, ws_bad_off, ws_bytes;
 };
 

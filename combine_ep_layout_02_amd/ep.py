@@ -12,6 +12,7 @@ from __future__ import annotations
 import ctypes
 import os
 from dataclasses import dataclass
+from functools import cached_property
 from typing import Optional
 
 import torch
@@ -59,6 +60,20 @@ class EpShape:
     def c(self) -> _Shape:
         return _Shape(self.num_tokens, self.hidden, self.num_topk, self.num_experts, self.num_ranks,
                       self.expert_alignment, self.capacity)
+
+    @cached_property
+    def c_ref(self):
+        """A ctypes pointer to this shape's ep_shape_t (built once, kept alive here)."""
+        self.__dict__["_c_keep"] = self.c()
+        return ctypes.byref(self.__dict__["_c_keep"])
+
+    @cached_property
+    def recv_rows(self) -> int:
+        return ep_recv_rows(self)
+
+    @cached_property
+    def workspace_bytes(self) -> int:
+        return ep_layout_workspace_bytes(self)
 
 
 def library_path() -> str:
@@ -218,6 +233,69 @@ def ep_check_cvt_bf16(inp, out, stream=None) -> None:
 
 
 # ---------------------------------------------------------------------------
+# Prepared calls: validate the arguments once, then launch with the stored
+# pointers (for loops that call the same entry point on the same buffers).
+# ---------------------------------------------------------------------------
+
+class Prepared:
+    """One entry point bound to fixed, already checked arguments."""
+    __slots__ = ("name", "_fn", "_args", "_keep")
+
+    def __init__(self, name, fn, args, keep):
+        self.name, self._fn, self._args, self._keep = name, fn, args, keep
+
+    def __call__(self, stream=None) -> None:
+        status = self._fn(*self._args, _stream(stream))
+        if status != EP_OK:
+            _check(self.name, status)
+
+
+def prepare_layout(shape: EpShape, topk_idx, expert_count, expert_offset, rank_count, rank_offset, slot,
+                   src_pair=None, diag=None, workspace=None) -> Prepared:
+    T, k, E, R = shape.num_tokens, shape.num_topk, shape.num_experts, shape.num_ranks
+    rows, ws_bytes = shape.recv_rows, shape.workspace_bytes
+    i32 = torch.int32
+    args = (
+        _ptr(topk_idx, "topk_idx", i32, T * k, optional=T == 0),
+        _ptr(expert_count, "expert_count", i32, E), _ptr(expert_offset, "expert_offset", i32, E + 1),
+        _ptr(rank_count, "rank_count", i32, R), _ptr(rank_offset, "rank_offset", i32, R + 1),
+        _ptr(slot, "slot", i32, T * k, optional=T == 0),
+        _ptr(src_pair, "src_pair", i32, rows, optional=True), _ptr(diag, "diag", i32, 2, optional=True),
+        _ptr(workspace, "workspace", None, None),
+    )
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < ws_bytes:
+        raise ValueError(f"workspace has {nbytes} bytes, needs {ws_bytes}")
+    keep = (topk_idx, expert_count, expert_offset, rank_count, rank_offset, slot, src_pair, diag, workspace)
+    return Prepared("ep_layout", lib().ep_layout, (shape.c_ref, *args, nbytes), keep)
+
+
+def prepare_dispatch(shape: EpShape, x, slot, recv_dtype: int, recv_x, recv_scale=None) -> Prepared:
+    T, H, k = shape.num_tokens, shape.hidden, shape.num_topk
+    rows = shape.recv_rows
+    if recv_dtype == EP_BF16:
+        rx, rs = _ptr(recv_x, "recv_x", _BF16_LIKE, rows * H), None
+    elif recv_dtype == EP_FP8_E4M3:
+        rx = _ptr(recv_x, "recv_x", _BYTE_LIKE, rows * H)
+        rs = _ptr(recv_scale, "recv_scale", torch.float32, rows * (H // 128))
+    else:
+        raise ValueError(f"unknown recv_dtype {recv_dtype}")
+    args = (shape.c_ref, _ptr(x, "x", _BF16_LIKE, T * H, optional=T == 0),
+            _ptr(slot, "slot", torch.int32, T * k, optional=T == 0), int(recv_dtype), rx, rs)
+    return Prepared("ep_dispatch", lib().ep_dispatch, args, (x, slot, recv_x, recv_scale))
+
+
+def prepare_combine(shape: EpShape, y, slot, topk_weights, out) -> Prepared:
+    T, H, k = shape.num_tokens, shape.hidden, shape.num_topk
+    rows = shape.recv_rows
+    args = (shape.c_ref, _ptr(y, "y", _BF16_LIKE, rows * H, optional=T == 0),
+            _ptr(slot, "slot", torch.int32, T * k, optional=T == 0),
+            _ptr(topk_weights, "topk_weights", torch.float32, T * k, optional=T == 0),
+            _ptr(out, "out", _BF16_LIKE, T * H, optional=T == 0))
+    return Prepared("ep_combine", lib().ep_combine, args, (y, slot, topk_weights, out))
+
+
+# ---------------------------------------------------------------------------
 # Convenience: allocate outputs with torch, then call the entry points above.
 # ---------------------------------------------------------------------------
 
@@ -243,13 +321,16 @@ class LayoutBuffers:
             shape, torch.empty(E, **i32), torch.empty(E + 1, **i32), torch.empty(R, **i32),
             torch.empty(R + 1, **i32), torch.empty((shape.num_tokens, shape.num_topk), **i32),
             torch.empty(ep_recv_rows(shape), **i32), torch.empty(2, **i32),
-            # zero-filled once; ep_layout leaves it zeroed after every call
-            torch.zeros((ws + 15) // 16 * 4, **i32))
+            torch.empty((ws + 15) // 16 * 4, **i32))
 
     def run(self, topk_idx: torch.Tensor, stream=None) -> "LayoutBuffers":
         ep_layout(self.shape, topk_idx, self.expert_count, self.expert_offset, self.rank_count,
                   self.rank_offset, self.slot, self.src_pair, self.diag, self.workspace, stream)
         return self
+
+    def prepare(self, topk_idx: torch.Tensor) -> Prepared:
+        return prepare_layout(self.shape, topk_idx, self.expert_count, self.expert_offset, self.rank_count,
+                              self.rank_offset, self.slot, self.src_pair, self.diag, self.workspace)
 
 
 def alloc_recv(shape: EpShape, recv_dtype: int, device="cuda"):

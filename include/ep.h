@@ -106,10 +106,9 @@ typedef enum ep_status_t {
 ep_status_t ep_recv_rows(const ep_shape_t *shape, int64_t *rows);
 
 /*
- * Bytes of device workspace ep_layout needs for `shape`.  Host only.
- * The workspace must be zero-filled once before its first use; every
- * ep_layout call leaves it zeroed again for the next one.  One workspace
- * must not be used by two ep_layout calls that may overlap in time.
+ * Bytes of device workspace ep_layout needs for `shape` (per-tile counts;
+ * no initial contents required).  Host only.  One workspace must not be
+ * used by two ep_layout calls that may overlap in time.
  */
 ep_status_t ep_layout_workspace_bytes(const ep_shape_t *shape, size_t *bytes);
 

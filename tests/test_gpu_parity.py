@@ -221,6 +221,10 @@ DISPATCH_EDGE = [
     ("h2176_padded", 200, 2176, 6, 32, 8, 1, 30, 0.0),
     ("k1", 257, 1024, 1, 4, 2, 1, 0, 0.0),
     ("k16_generic", 64, 512, 16, 64, 8, 1, 0, 0.1),
+    ("h3584_odd_chunks", 100, 3584, 8, 32, 8, 1, 0, 0.0),
+    ("h640_partial_chunk", 200, 640, 2, 8, 2, 1, 0, 0.0),
+    ("h9216_two_slices", 40, 9216, 4, 16, 4, 1, 0, 0.05),
+    ("h16384_two_slices", 24, 16384, 3, 12, 3, 1, 0, 0.0),
 ]
 
 

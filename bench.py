@@ -10,11 +10,24 @@ is algorithmic bytes per step (layout + dispatch + combine, counted as the
 method must move them) times K over the wall time of K steps.
 
 Also reported: per-stage kernel times from HIP events recorded around each
-stage inside the timed loop, the roofline of the dominant kernel (combine,
+call in a second timed loop, the roofline of the dominant kernel (combine,
 HBM-bound), the decode-shaped workload's microseconds per call, and the CPU
 oracle timed on this host (one thread) on the same workload.
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
+
+Measured HBM traffic of the combine kernel comes from two rocprofv3 counter
+runs of this script (FETCH_SIZE, then WRITE_SIZE) with --calibration-copy,
+which adds a plain 1 GiB device copy whose true byte counts scale the
+counters:
+
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d F -- python3 bench.py --steps 3 --warmup 1 --no-decode --no-cpu-baseline --calibration-copy
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d W -- python3 bench.py --steps 3 --warmup 1 --no-decode --no-cpu-baseline --calibration-copy
+    python3 bench.py --traffic-from F W
+
+The last command writes profiles/combine_v3_traffic.json, stamped with a hash
+of the combine kernel's source; the traffic figure is reported only while
+that source is unchanged.
 """
 from __future__ import annotations
 
@@ -103,17 +116,26 @@ class Step:
 
 
 def time_steps(step, steps, warmup):
-    """Warm up, then time `steps` steps with per-stage events on the launch stream."""
+    """Warm up, then time `steps` back-to-back steps between two HIP events on
+    the launch stream (torch's current stream, which the binding launches on)."""
     for _ in range(warmup):
         step.run()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
-    for i in range(steps):
-        e = ev[i]
+    for _ in range(steps):
+        step.run()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end), time.perf_counter() - t0
+
+
+def time_stages(step, steps):
+    """Per-stage kernel time: HIP events around each call, on the launch stream."""
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in ev:
         e[0].record()
         step.layout()
         e[1].record()
@@ -121,12 +143,8 @@ def time_steps(step, steps, warmup):
         e[2].record()
         step.combine()
         e[3].record()
-    end.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])  # ms
-    return total_ms, wall, stage
+    return np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])  # ms
 
 
 def source_hash():
@@ -154,6 +172,58 @@ def measured_traffic():
 # CPU oracle baseline
 # --------------------------------------------------------------------------
 
+def calibration_copy(dev, reps=3):
+    """A plain streaming elementwise kernel of exactly 1 GiB read and 1 GiB written
+    (bitwise NOT of 2^29 int16); returns its median GB/s (read + written bytes)."""
+    a = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+    b = torch.empty_like(a)
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.bitwise_not(a, out=b)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del a, b
+    return 2 * (1 << 30) / (float(np.median(ms)) / 1e3) / 1e9
+
+
+def traffic_from(fetch_dir, write_dir):
+    """Combine-kernel HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
+    each scaled by what the same counter reads for the 1 GiB calibration copy."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        out = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                key = "combine" if "combine_kernel" in name else "copy" if "bitwise_not" in name else None
+                if key:
+                    out.setdefault(key, []).append(float(r["Counter_Value"]))
+        return out
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+    f_scale = gib_kib / float(np.median(fetch["copy"]))
+    w_scale = gib_kib / float(np.median(write["copy"]))
+    fb = float(np.median(fetch["combine"])) * f_scale * 1024
+    wb = float(np.median(write["combine"])) * w_scale * 1024
+    rec = {"kernel": "combine_kernel<8, NT, NT> on the 8192-token workload", "source_hash": source_hash(),
+           "fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
+           "algorithmic_bytes_per_launch": bytes_combine(wl.WORKLOADS["v3"]),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "raw_fetch_kib": float(np.median(fetch["combine"])), "raw_write_kib": float(np.median(write["combine"])),
+           "copy_fetch_kib": float(np.median(fetch["copy"])), "copy_write_kib": float(np.median(write["copy"]))}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(step):
     import oracle  # test infrastructure; only this leg of the benchmark uses it
     w, inp = step.w, step.inp
@@ -178,7 +248,14 @@ def main():
     ap.add_argument("--workload", default="v3", choices=["v3", "skew"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="counter runs: keep the 1 GiB calibration copy to 3 launches")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 counter runs into profiles/combine_v3_traffic.json and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU's share of the path; it has no multi-GPU mode "
@@ -193,23 +270,30 @@ def main():
     log(f"[bench] generating {w.name} inputs")
     step = Step(w, dev, fp8=True)
     log(f"[bench] timing {args.steps} steps after {args.warmup} warm-up")
-    total_ms, wall, stage = time_steps(step, args.steps, args.warmup)
+    total_ms, wall = time_steps(step, args.steps, args.warmup)
     ms_per_step = total_ms / args.steps
     value = step.bytes * args.steps / (total_ms / 1e3) / 1e9
+    stage = time_stages(step, args.steps)
     lay_ms, disp_ms, comb_ms = stage.mean(axis=0)
 
     dec = None
     if not args.no_decode:
         log("[bench] decode workload")
         dstep = Step(wl.WORKLOADS["decode"], dev, fp8=True)
-        d_total, _, d_stage = time_steps(dstep, 200, 20)
-        dec = {"us_per_call": round(d_total / 200 * 1e3, 2),
-               "layout_us": round(float(d_stage[:, 0].mean()) * 1e3, 2),
-               "dispatch_us": round(float(d_stage[:, 1].mean()) * 1e3, 2),
-               "combine_us": round(float(d_stage[:, 2].mean()) * 1e3, 2),
-               "bytes": dstep.bytes, "note": "warm (inputs stay in the 256 MB Infinity Cache), back-to-back"}
+        n = 500
+        d_total, _ = time_steps(dstep, n, 50)
+        d_stage = time_stages(dstep, 100)
+        dec = {"us_per_call": round(d_total / n * 1e3, 2),
+               "layout_us": round(float(np.median(d_stage[:, 0])) * 1e3, 2),
+               "dispatch_us": round(float(np.median(d_stage[:, 1])) * 1e3, 2),
+               "combine_us": round(float(np.median(d_stage[:, 2])) * 1e3, 2),
+               "bytes": dstep.bytes,
+               "note": "one call = layout + FP8 dispatch + combine of 128 tokens into the padded [256, 128, 7168] "
+                       "layout; mean over 500 back-to-back calls (inputs stay in the 256 MB Infinity Cache); "
+                       "stage times are medians with events around each kernel"}
         del dstep
 
+    copy_gbps = calibration_copy(dev, reps=3 if args.calibration_copy else 5)
     cb = None if args.no_cpu_baseline else cpu_baseline(step)
 
     comb_bytes = bytes_combine(w)
@@ -242,6 +326,8 @@ def main():
         "roofline": {"kernel": "combine", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": comb_bytes},
+        "copy_ceiling": {"GBps": round(copy_gbps, 1), "kernel": "torch bitwise_not, 1 GiB in + 1 GiB out",
+                         "step_frac_of_copy": round(value / copy_gbps, 4)},
         "decode": dec,
         "cpu_baseline": cb,
         "wall_s_timed": round(wall, 4),

@@ -32,7 +32,7 @@
 namespace ep {
 namespace {
 
-constexpr int kMaxChunks = 16;     // 512-column chunks held per wavefront (8192 columns)
+constexpr int kMaxChunks = 16;     // most 512-column chunks a wavefront holds (8192 columns)
 constexpr int kWavesPerBlock = 4;  // 256 threads
 constexpr int kMinWaves = 2048;    // 8 wavefronts per CU
 constexpr uint32_t kNoColumn = 0xFFFFFFF0u;  // a load offset past any row: reads 0
@@ -60,22 +60,23 @@ __device__ __forceinline__ bool slice_of(const RowParams& p, int wpt, int cpw, i
   return true;
 }
 
-template <int AUX_LD>
-__device__ __forceinline__ void load_row(const RowParams& p, const Slice& sl, int lane, u32x4 (&v)[kMaxChunks]) {
+template <int NC, int AUX_LD>
+__device__ __forceinline__ void load_row(const RowParams& p, const Slice& sl, int lane, u32x4 (&v)[NC]) {
   const uint16_t* xrow = static_cast<const uint16_t*>(p.src) + (int64_t)sl.t * p.H;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(xrow, (uint32_t)p.H * 2u);
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c)
+  for (int c = 0; c < NC; ++c)
     v[c] = load16<AUX_LD>(rx, c < sl.nc ? (uint32_t)((sl.c0 + c) * 512 + lane * 8) * 2u : kNoColumn);
 }
 
-template <int AUX_LD, int AUX_ST>
+// NC: chunk capacity of the instantiation (>= chunks per wavefront).
+template <int NC, int AUX_LD, int AUX_ST>
 __global__ __launch_bounds__(256) void dispatch_bf16_kernel(RowParams p, int wpt, int cpw, int nchunks) {
   const int lane = threadIdx.x & 63;
   Slice sl;
   if (!slice_of(p, wpt, cpw, nchunks, sl)) return;
-  u32x4 v[kMaxChunks];
-  load_row<AUX_LD>(p, sl, lane, v);
+  u32x4 v[NC];
+  load_row<NC, AUX_LD>(p, sl, lane, v);
   const int slots = load_lane_slot(p.slot, sl.t, p.k, lane);
 
   uint16_t* dst = static_cast<uint16_t*>(p.dst);
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(256) void dispatch_bf16_kernel(RowParams p, int wpt
     if (!slot_ok(s, p.rows)) continue;
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(dst + (int64_t)s * p.H, (uint32_t)p.H * 2u);
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c)
+    for (int c = 0; c < NC; ++c)
       if (c < sl.nc) store16<AUX_ST>(rd, col + 1024u * c, v[c]);
   }
 }
@@ -110,26 +111,27 @@ __device__ __forceinline__ float block_scale(uint32_t amax_bits16) {
 // even lane of a lane pair stores 16 bytes of chunk 2m, the odd lane the same
 // bytes of chunk 2m+1.  A pair whose second chunk lies past the row stores
 // that half out of range, where the store is dropped.
-template <int AUX_LD, int AUX_ST>
+template <int NC, int AUX_LD, int AUX_ST>
 __global__ __launch_bounds__(256) void dispatch_fp8_kernel(RowParams p, int wpt, int cpw, int nchunks) {
+  static_assert(NC % 2 == 0, "chunks pair up");
   const int lane = threadIdx.x & 63;
   Slice sl;
   if (!slice_of(p, wpt, cpw, nchunks, sl)) return;
-  u32x4 v[kMaxChunks];
-  load_row<AUX_LD>(p, sl, lane, v);
+  u32x4 v[NC];
+  load_row<NC, AUX_LD>(p, sl, lane, v);
   const int slots = load_lane_slot(p.slot, sl.t, p.k, lane);
 
-  float sc[kMaxChunks];
-  u32x2 q[kMaxChunks];
+  float sc[NC];
+  u32x2 q[NC];
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
+  for (int c = 0; c < NC; ++c) {
     sc[c] = block_scale(row16_max_u32(absmax_bits8(v[c])));
     q[c] = quantize8(v[c], sc[c]);
   }
   const bool odd = lane & 1;
-  u32x4 out[kMaxChunks / 2];
+  u32x4 out[NC / 2];
 #pragma unroll
-  for (int m = 0; m < kMaxChunks / 2; ++m) {
+  for (int m = 0; m < NC / 2; ++m) {
     const u32x2 a = q[2 * m], b = q[2 * m + 1];
     const u32x2 send = odd ? a : b;
     u32x2 recv;
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(256) void dispatch_fp8_kernel(RowParams p, int wpt,
   float my_scale = 0.0f;
   const int owner = (lane & 3) << 4;
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
+  for (int c = 0; c < NC; ++c) {
     const float g = __shfl(sc[c], owner, 64);
     if ((lane >> 2) == c) my_scale = g;
   }
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(256) void dispatch_fp8_kernel(RowParams p, int wpt,
     if (!slot_ok(s, p.rows)) continue;
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(dst + (int64_t)s * H, (uint32_t)H);
 #pragma unroll
-    for (int m = 0; m < kMaxChunks / 2; ++m)
+    for (int m = 0; m < NC / 2; ++m)
       if (2 * m < sl.nc) store16<AUX_ST>(rd, ocol + 1024u * m, out[m]);
     if (lane < 4 * sl.nc) {
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.recv_scale + (int64_t)s * nb, (uint32_t)nb * 4u);
@@ -214,27 +216,52 @@ Split split_for(const RowParams& p) {
 
 }  // namespace
 
+namespace {
+
+template <int NC>
+void launch_bf16_nc(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  if (streaming)
+    hipLaunchKernelGGL((dispatch_bf16_kernel<NC, kAuxDefault, kAuxNT>), dim3(s.blocks), dim3(256), 0, stream, p,
+                       s.wpt, s.cpw, s.nchunks);
+  else
+    hipLaunchKernelGGL((dispatch_bf16_kernel<NC, kAuxDefault, kAuxDefault>), dim3(s.blocks), dim3(256), 0, stream,
+                       p, s.wpt, s.cpw, s.nchunks);
+}
+
+template <int NC>
+void launch_fp8_nc(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  if (streaming)
+    hipLaunchKernelGGL((dispatch_fp8_kernel<NC, kAuxDefault, kAuxNT>), dim3(s.blocks), dim3(256), 0, stream, p,
+                       s.wpt, s.cpw, s.nchunks);
+  else
+    hipLaunchKernelGGL((dispatch_fp8_kernel<NC, kAuxDefault, kAuxDefault>), dim3(s.blocks), dim3(256), 0, stream,
+                       p, s.wpt, s.cpw, s.nchunks);
+}
+
+}  // namespace
+
+// The instantiation used is the smallest chunk capacity in {2, 4, 8, 16}
+// that holds a wavefront's chunks, so narrow slices carry no dead registers
+// or instructions.
 hipError_t launch_dispatch_bf16(const RowParams& p, hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
   const Split s = split_for(p);
-  if ((int64_t)p.T * p.k * p.H * 2 >= kStreamingBytes)
-    hipLaunchKernelGGL((dispatch_bf16_kernel<kAuxDefault, kAuxNT>), dim3(s.blocks), dim3(256), 0, stream, p, s.wpt,
-                       s.cpw, s.nchunks);
-  else
-    hipLaunchKernelGGL((dispatch_bf16_kernel<kAuxDefault, kAuxDefault>), dim3(s.blocks), dim3(256), 0, stream, p,
-                       s.wpt, s.cpw, s.nchunks);
+  const bool streaming = (int64_t)p.T * p.k * p.H * 2 >= kStreamingBytes;
+  if (s.cpw <= 2) launch_bf16_nc<2>(s, p, streaming, stream);
+  else if (s.cpw <= 4) launch_bf16_nc<4>(s, p, streaming, stream);
+  else if (s.cpw <= 8) launch_bf16_nc<8>(s, p, streaming, stream);
+  else launch_bf16_nc<16>(s, p, streaming, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_dispatch_fp8(const RowParams& p, hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
   const Split s = split_for(p);
-  if ((int64_t)p.T * p.k * p.H >= kStreamingBytes)
-    hipLaunchKernelGGL((dispatch_fp8_kernel<kAuxDefault, kAuxNT>), dim3(s.blocks), dim3(256), 0, stream, p, s.wpt,
-                       s.cpw, s.nchunks);
-  else
-    hipLaunchKernelGGL((dispatch_fp8_kernel<kAuxDefault, kAuxDefault>), dim3(s.blocks), dim3(256), 0, stream, p,
-                       s.wpt, s.cpw, s.nchunks);
+  const bool streaming = (int64_t)p.T * p.k * p.H >= kStreamingBytes;
+  if (s.cpw <= 2) launch_fp8_nc<2>(s, p, streaming, stream);
+  else if (s.cpw <= 4) launch_fp8_nc<4>(s, p, streaming, stream);
+  else if (s.cpw <= 8) launch_fp8_nc<8>(s, p, streaming, stream);
+  else launch_fp8_nc<16>(s, p, streaming, stream);
   return hipGetLastError();
 }
 

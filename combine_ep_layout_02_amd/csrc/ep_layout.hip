@@ -120,38 +120,48 @@ __device__ void fill_padding_rows(const LayoutParams& p, const int* tot, const i
 
 }  // namespace
 
-// One block per tile of tokens, 64*W threads, one pair per thread.  With a
-// single tile, `gridDim.x` blocks each rebuild the (small) layout in LDS and
-// share the output writes, so no block waits for another.
+// LDS of the tile pass (dynamic shared memory, carved in this order).
 template <int W>
-__global__ __launch_bounds__(64 * W) void layout_tiles_kernel(LayoutParams p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int E = p.E, R = p.R, k = p.k;
-  uint64_t* masks = reinterpret_cast<uint64_t*>(smem);     // [W][E]
-  uint64_t* tokrank = masks + (size_t)W * E;               // [64*W] ranks hit per token (R <= 64)
-  int* pref = reinterpret_cast<int*>(tokrank + 64 * W);    // [W][E] pairs of e in earlier windows
-  int* idx_s = pref + (size_t)W * E;                       // [64*W]
-  int* rank_of = idx_s + 64 * W;                           // [E]
-  int* rank_hist = rank_of + E;                            // [R]
-  int* cnt_s = rank_hist + R;                              // [E]
-  int* offs = cnt_s + E;                                   // [E+1]
-  __shared__ int s_bad;
-  __shared__ int s_part[20];
+struct TileLds {
+  uint64_t* masks;    // [W][E]   pairs of expert e in window w, one bit per lane
+  uint64_t* tokrank;  // [64*W]   ranks hit by each token of the tile (R <= 64)
+  int* pref;          // [W][E]   pairs of expert e in earlier windows
+  int* idx_s;         // [64*W]   expert of each pair (-1 if none)
+  int* rank_of;       // [E]      rank owning each expert
+  int* rank_hist;     // [R]      distinct tokens per rank
+  int* cnt_s;         // [E]      pairs per expert
+  int* offs;          // [E+1]    offsets (single-tile path)
+  __device__ TileLds(unsigned char* smem, int E, int R) {
+    masks = reinterpret_cast<uint64_t*>(smem);
+    tokrank = masks + (size_t)W * E;
+    pref = reinterpret_cast<int*>(tokrank + 64 * W);
+    idx_s = pref + (size_t)W * E;
+    rank_of = idx_s + 64 * W;
+    rank_hist = rank_of + E;
+    cnt_s = rank_hist + R;
+    offs = cnt_s + E;
+  }
+};
 
+// Counts and stable in-tile ranks of one tile, one pair per thread.  Leaves
+// cnt_s / rank_hist / *s_bad in LDS and returns the thread's expert (or -1)
+// and in-tile rank.  Ends with a barrier.
+template <int W>
+__device__ void tile_pass(const LayoutParams& p, const TileLds<W>& L, int tile, int* s_bad, int& e_out,
+                          int& local_out) {
+  const int E = p.E, R = p.R, k = p.k;
   const int tid = threadIdx.x, nthr = 64 * W;
-  const bool single = p.ntiles == 1;
-  const int tile = single ? 0 : blockIdx.x;
   const int t0 = tile * p.TT;
   const int nt = max(0, min(p.TT, p.T - t0));
   const int np = nt * k;
   const int64_t g0 = (int64_t)t0 * k;
   const bool small_r = R <= 64;
 
-  for (int i = tid; i < W * E; i += nthr) masks[i] = 0;
-  tokrank[tid] = 0;
-  for (int i = tid; i < E; i += nthr) rank_of[i] = udiv((uint32_t)i, p.magic_per);
-  for (int i = tid; i < R; i += nthr) rank_hist[i] = 0;
-  if (tid == 0) s_bad = 0;
+  for (int i = tid; i < W * E; i += nthr) L.masks[i] = 0;
+  L.tokrank[tid] = 0;
+  for (int i = tid; i < E; i += nthr) L.rank_of[i] = udiv((uint32_t)i, p.magic_per);
+  for (int i = tid; i < R; i += nthr) L.rank_hist[i] = 0;
+  if (tid == 0) *s_bad = 0;
   __syncthreads();
 
   int e = -1;
@@ -161,16 +171,16 @@ __global__ __launch_bounds__(64 * W) void layout_tiles_kernel(LayoutParams p) {
     if (v >= 0 && v < E) e = v;
     else bad = (v != -1);
   }
-  idx_s[tid] = e;
+  L.idx_s[tid] = e;
   const int w = tid >> 6, lane = tid & 63;
   const int tl = udiv((uint32_t)tid, p.magic_k);  // token of the pair inside the tile
   if (e >= 0) {
-    atomicOr(reinterpret_cast<unsigned long long*>(&masks[w * E + e]), 1ull << lane);
-    if (small_r) atomicOr(reinterpret_cast<unsigned long long*>(&tokrank[tl]), 1ull << rank_of[e]);
+    atomicOr(reinterpret_cast<unsigned long long*>(&L.masks[w * E + e]), 1ull << lane);
+    if (small_r) atomicOr(reinterpret_cast<unsigned long long*>(&L.tokrank[tl]), 1ull << L.rank_of[e]);
   }
   {
     const uint64_t bb = __ballot(bad);
-    if (lane == 0 && bb) atomicAdd(&s_bad, (int)__popcll(bb));
+    if (lane == 0 && bb) atomicAdd(s_bad, (int)__popcll(bb));
   }
   __syncthreads();
 
@@ -178,88 +188,46 @@ __global__ __launch_bounds__(64 * W) void layout_tiles_kernel(LayoutParams p) {
   for (int ee = tid; ee < E; ee += nthr) {
     int c[W];
 #pragma unroll
-    for (int w2 = 0; w2 < W; ++w2) c[w2] = (int)__popcll(masks[w2 * E + ee]);
+    for (int w2 = 0; w2 < W; ++w2) c[w2] = (int)__popcll(L.masks[w2 * E + ee]);
     int run = 0;
 #pragma unroll
-    for (int w2 = 0; w2 < W; ++w2) { pref[w2 * E + ee] = run; run += c[w2]; }
-    cnt_s[ee] = run;
+    for (int w2 = 0; w2 < W; ++w2) { L.pref[w2 * E + ee] = run; run += c[w2]; }
+    L.cnt_s[ee] = run;
   }
   // distinct tokens per rank
   if (small_r) {
     if (tid < nt) {
-      uint64_t m = tokrank[tid];
+      uint64_t m = L.tokrank[tid];
       while (m) {
-        atomicAdd(&rank_hist[__builtin_ctzll(m)], 1);
+        atomicAdd(&L.rank_hist[__builtin_ctzll(m)], 1);
         m &= m - 1;
       }
     }
   } else if (e >= 0) {
     // the token's first pair on a rank counts the token once for it
-    const int r = rank_of[e];
+    const int r = L.rank_of[e];
     bool first = true;
     for (int q = tl * k; q < tid; ++q) {
-      const int e2 = idx_s[q];
-      if (e2 >= 0 && rank_of[e2] == r) { first = false; break; }
+      const int e2 = L.idx_s[q];
+      if (e2 >= 0 && L.rank_of[e2] == r) { first = false; break; }
     }
-    if (first) atomicAdd(&rank_hist[r], 1);
+    if (first) atomicAdd(&L.rank_hist[r], 1);
   }
   __syncthreads();
 
   // rank of the pair among the tile's pairs of the same expert
-  const int local =
-      e >= 0 ? pref[w * E + e] + (int)__popcll(masks[w * E + e] & ((1ull << lane) - 1ull)) : -1;
-
-  if (single) {
-    // The whole batch is this tile.  Block 0 writes outputs and slots; all
-    // blocks share the padding rows.
-    const bool lead = blockIdx.x == 0;
-    if (lead && tid == 0 && p.diag) { p.diag[0] = s_bad; p.diag[1] = 0; }
-    scan_offsets(cnt_s, offs, E, p.A, p.C, s_part);  // barrier: diag[1] is zero before the adds
-    if (lead) {
-      write_outputs(p, cnt_s, offs, rank_hist);
-      if (tid < np) {
-        int s = -1;
-        if (e >= 0) {
-          s = slot_of(p, e, local, offs);
-          if (s >= 0 && p.src_pair) p.src_pair[s] = (int)(g0 + tid);
-        }
-        p.slot[g0 + tid] = s;
-      }
-    }
-    fill_padding_rows(p, cnt_s, offs, blockIdx.x * W + w, gridDim.x * W, lane,
-                      (int64_t)blockIdx.x * nthr + tid, (int64_t)gridDim.x * nthr);
-    return;
-  }
-
-  // Publish this tile's counts and in-tile ranks for the finalize kernel.
-  for (int ee = tid; ee < E; ee += nthr) p.ws_tile[(size_t)tile * E + ee] = cnt_s[ee];
-  for (int r = tid; r < R; r += nthr) p.ws_rank[(size_t)tile * R + r] = rank_hist[r];
-  if (tid == 0) p.ws_bad[tile] = s_bad;
-  if (tid < np) p.slot[g0 + tid] = local;
+  e_out = e;
+  local_out = e >= 0 ? L.pref[w * E + e] + (int)__popcll(L.masks[w * E + e] & ((1ull << lane) - 1ull)) : -1;
 }
 
-// One block per tile.  Rebuilds totals, offsets and this tile's prefix from
-// the per-tile counts, then turns the tile's in-tile ranks into slots.
-__global__ __launch_bounds__(1024) void layout_finalize_kernel(LayoutParams p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int E = p.E, R = p.R, G = p.G, ntiles = p.ntiles;
-  const int gE = max(G * E, E);
-  int* part_tot = reinterpret_cast<int*>(smem);  // [G][E]
-  int* part_pre = part_tot + gE;                 // [G][E]
-  int* tot = part_pre + gE;                      // [E]
-  int* pre = tot + E;                            // [E]
-  int* offs = pre + E;                           // [E+1]
-  int* rank_tot = offs + E + 1;                  // [R]
-  __shared__ int s_bad;
-  __shared__ int s_part[20];
-
+// Per-expert totals over all tiles and the part before `tile`, from the
+// [tiles x E] count matrix: (tile group, expert) jobs, loads in batches of
+// 16 independent reads, then a reduction over groups.  Ends with a barrier.
+__device__ void reduce_tiles(const LayoutParams& p, int tile, int G, int* part_tot, int* part_pre, int* tot,
+                             int* pre) {
+  const int E = p.E, ntiles = p.ntiles;
   const int tid = threadIdx.x, nthr = blockDim.x;
-  const int tile = blockIdx.x;
-  for (int r = tid; r < R; r += nthr) rank_tot[r] = 0;
-
-  // (a) per (tile group, expert): sum of the group's tile counts, and the
-  //     part of it that lies before this block's tile.  Loads go out in
-  //     batches of 16 independent reads.
+  const int gE = max(G * E, E);
   for (int job = tid; job < gE; job += nthr) {
     int g = 0, e = job;
     if (G > 1) { g = udiv((uint32_t)job, p.magic_E); e = job - g * E; }
@@ -281,7 +249,6 @@ __global__ __launch_bounds__(1024) void layout_finalize_kernel(LayoutParams p) {
     part_tot[g * E + e] = st;
     part_pre[g * E + e] = sp;
   }
-  if (tid == 0) s_bad = 0;
   __syncthreads();
   for (int e = tid; e < E; e += nthr) {
     int st = 0, sp = 0;
@@ -289,23 +256,103 @@ __global__ __launch_bounds__(1024) void layout_finalize_kernel(LayoutParams p) {
     tot[e] = st;
     pre[e] = sp;
   }
-  if (tile == 0) {
-    // rank counts and invalid ids: coalesced sweeps, LDS atomics
-    for (int i = tid; i < ntiles * R; i += nthr) {
-      const int v = p.ws_rank[i];
-      if (v) atomicAdd(&rank_tot[i - udiv((uint32_t)i, p.magic_R) * R], v);
-    }
-    int bad = 0;
-    for (int t = tid; t < ntiles; t += nthr) bad += p.ws_bad[t];
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) bad += __shfl_xor(bad, d, 64);
-    if ((tid & 63) == 0 && bad) atomicAdd(&s_bad, bad);
-  }
   __syncthreads();
-  if (tile == 0 && tid == 0 && p.diag) { p.diag[0] = s_bad; p.diag[1] = 0; }
-  scan_offsets(tot, offs, E, p.A, p.C, s_part);  // barrier: diag[1] is zero before the adds
+}
 
-  // (b) this tile's slots
+// Block 0 only: rank counts and invalid ids summed over tiles (coalesced
+// sweeps, LDS atomics); rank_tot must be zero.  Ends with a barrier.
+__device__ void reduce_ranks(const LayoutParams& p, int* rank_tot, int* s_bad) {
+  const int R = p.R, ntiles = p.ntiles;
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  for (int i = tid; i < ntiles * R; i += nthr) {
+    const int v = p.ws_rank[i];
+    if (v) atomicAdd(&rank_tot[i - udiv((uint32_t)i, p.magic_R) * R], v);
+  }
+  int bad = 0;
+  for (int t = tid; t < ntiles; t += nthr) bad += p.ws_bad[t];
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) bad += __shfl_xor(bad, d, 64);
+  if ((tid & 63) == 0 && bad) atomicAdd(s_bad, bad);
+  __syncthreads();
+}
+
+// Tile pass.  With a single tile, gridDim.x blocks each rebuild the (small)
+// layout in LDS and share the output writes, so no block waits for another.
+// With several tiles it publishes the tile's counts and in-tile ranks for
+// layout_finalize_kernel.
+template <int W>
+__global__ __launch_bounds__(64 * W) void layout_tiles_kernel(LayoutParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_bad;
+  __shared__ int s_part[20];
+  const TileLds<W> L(smem, p.E, p.R);
+  const int tid = threadIdx.x, nthr = 64 * W;
+  const bool single = p.ntiles == 1;
+  const int tile = single ? 0 : blockIdx.x;
+  const int64_t g0 = (int64_t)tile * p.TT * p.k;
+  const int np = max(0, min(p.TT, p.T - tile * p.TT)) * p.k;
+  int e, local;
+  tile_pass<W>(p, L, tile, &s_bad, e, local);
+
+  if (single) {
+    // Block 0 writes outputs and slots; all blocks share the padding rows.
+    const bool lead = blockIdx.x == 0;
+    if (lead && tid == 0 && p.diag) { p.diag[0] = s_bad; p.diag[1] = 0; }
+    scan_offsets(L.cnt_s, L.offs, p.E, p.A, p.C, s_part);  // barrier: diag[1] is zero before the adds
+    if (lead) {
+      write_outputs(p, L.cnt_s, L.offs, L.rank_hist);
+      if (tid < np) {
+        int s = -1;
+        if (e >= 0) {
+          s = slot_of(p, e, local, L.offs);
+          if (s >= 0 && p.src_pair) p.src_pair[s] = (int)(g0 + tid);
+        }
+        p.slot[g0 + tid] = s;
+      }
+    }
+    fill_padding_rows(p, L.cnt_s, L.offs, blockIdx.x * W + (tid >> 6), gridDim.x * W, tid & 63,
+                      (int64_t)blockIdx.x * nthr + tid, (int64_t)gridDim.x * nthr);
+    return;
+  }
+
+  for (int ee = tid; ee < p.E; ee += nthr) p.ws_tile[(size_t)tile * p.E + ee] = L.cnt_s[ee];
+  for (int r = tid; r < p.R; r += nthr) p.ws_rank[(size_t)tile * p.R + r] = L.rank_hist[r];
+  if (tid == 0) p.ws_bad[tile] = s_bad;
+  if (tid < np) p.slot[g0 + tid] = local;
+}
+
+// Finalize LDS, carved from the front of the dynamic shared memory.
+struct FinLds {
+  int *part_tot, *part_pre, *tot, *pre, *offs, *rank_tot;
+  __device__ FinLds(unsigned char* smem, int G, int E) {
+    const int gE = max(G * E, E);
+    part_tot = reinterpret_cast<int*>(smem);
+    part_pre = part_tot + gE;
+    tot = part_pre + gE;
+    pre = tot + E;
+    offs = pre + E;
+    rank_tot = offs + E + 1;
+  }
+};
+
+// One block per tile.  Rebuilds totals, offsets and this tile's prefix from
+// the per-tile counts, then turns the tile's in-tile ranks into slots.
+__global__ __launch_bounds__(1024) void layout_finalize_kernel(LayoutParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_bad;
+  __shared__ int s_part[20];
+  const int E = p.E, R = p.R;
+  const FinLds F(smem, p.G, E);
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int tile = blockIdx.x;
+  for (int r = tid; r < R; r += nthr) F.rank_tot[r] = 0;
+  if (tid == 0) s_bad = 0;
+  reduce_tiles(p, tile, p.G, F.part_tot, F.part_pre, F.tot, F.pre);
+  if (tile == 0) reduce_ranks(p, F.rank_tot, &s_bad);
+  if (tile == 0 && tid == 0 && p.diag) { p.diag[0] = s_bad; p.diag[1] = 0; }
+  scan_offsets(F.tot, F.offs, E, p.A, p.C, s_part);  // barrier: diag[1] is zero before the adds
+
+  // this tile's slots
   {
     const int t0 = tile * p.TT;
     const int np = max(0, min(p.TT, p.T - t0)) * p.k;
@@ -313,19 +360,15 @@ __global__ __launch_bounds__(1024) void layout_finalize_kernel(LayoutParams p) {
     for (int i = tid; i < np; i += nthr) {
       const int v = p.idx[g0 + i];
       if (!(v >= 0 && v < E)) continue;  // slot already -1
-      int s = slot_of(p, v, pre[v] + p.slot[g0 + i], offs);
+      int s = slot_of(p, v, F.pre[v] + p.slot[g0 + i], F.offs);
       if ((int64_t)s >= p.rows) s = -1;  // cannot happen; keeps every write in bounds
       p.slot[g0 + i] = s;
       if (s >= 0 && p.src_pair) p.src_pair[s] = (int)(g0 + i);
     }
   }
-
-  // (c) block 0: counts, offsets, rank counts, dropped pairs
-  if (tile == 0) write_outputs(p, tot, offs, rank_tot);
-
-  // (d) padding rows, experts spread over all wavefronts of the grid
+  if (tile == 0) write_outputs(p, F.tot, F.offs, F.rank_tot);
   const int nw = nthr >> 6;
-  fill_padding_rows(p, tot, offs, tile * nw + (tid >> 6), gridDim.x * nw, tid & 63,
+  fill_padding_rows(p, F.tot, F.offs, tile * nw + (tid >> 6), gridDim.x * nw, tid & 63,
                     (int64_t)tile * nthr + tid, (int64_t)gridDim.x * nthr);
 }
 
@@ -353,8 +396,11 @@ LayoutPlan plan_layout(int T, int k, int E, int R) {
   pl.lds_bytes = tile_lds(pl.W);
   pl.fin_threads = 1024;
   pl.G = E <= pl.fin_threads ? max(1, min(pl.fin_threads / E, pl.ntiles)) : 1;
-  const size_t gE = (size_t)(pl.G * E > E ? pl.G * E : E);
-  pl.fin_lds_bytes = (size_t)4 * (2 * gE + 3 * (size_t)E + 1 + R);
+  auto fin_lds = [&](int G) {
+    const size_t gE = (size_t)(G * E > E ? G * E : E);
+    return (size_t)4 * (2 * gE + 3 * (size_t)E + 1 + R);
+  };
+  pl.fin_lds_bytes = fin_lds(pl.G);
   pl.ws_tile_off = 0;
   pl.ws_rank_off = pl.ws_tile_off + (((size_t)pl.ntiles * E * 4 + 255) & ~(size_t)255);
   pl.ws_bad_off = pl.ws_rank_off + (((size_t)pl.ntiles * R * 4 + 255) & ~(size_t)255);
@@ -362,11 +408,20 @@ LayoutPlan plan_layout(int T, int k, int E, int R) {
   return pl;
 }
 
+namespace {
+
+template <int W>
+hipError_t launch_tiles(const LayoutPlan& pl, LayoutParams& p, int blocks, hipStream_t stream) {
+  hipLaunchKernelGGL(layout_tiles_kernel<W>, dim3(blocks), dim3(pl.threads), pl.lds_bytes, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_layout(const LayoutPlan& pl, LayoutParams p, hipStream_t stream) {
   p.W = pl.W;
   p.TT = pl.TT;
   p.ntiles = pl.ntiles;
-  p.G = pl.G;
   // Exact for every quotient taken: pair index < 1024 over k <= 64, expert id
   // < 2048 over E/R <= 2048, job index < 2048 over E <= 2048, workspace index
   // < 2^22 over R <= 2048 (n * d < 2^32 in each case).
@@ -374,17 +429,19 @@ hipError_t launch_layout(const LayoutPlan& pl, LayoutParams p, hipStream_t strea
   p.magic_per = magic_for((uint32_t)(p.E / p.R));
   p.magic_E = magic_for((uint32_t)p.E);
   p.magic_R = magic_for((uint32_t)p.R);
+
   // One tile: several blocks rebuild it and share the padding rows of src_pair.
   int blocks = pl.ntiles;
   if (pl.ntiles == 1 && p.src_pair) blocks = (int)std::min<int64_t>(16, std::max<int64_t>(1, p.rows / 4096));
+  p.G = pl.G;
+  hipError_t err;
   switch (pl.W) {
-    case 16: hipLaunchKernelGGL(layout_tiles_kernel<16>, dim3(blocks), dim3(pl.threads), pl.lds_bytes, stream, p); break;
-    case 8: hipLaunchKernelGGL(layout_tiles_kernel<8>, dim3(blocks), dim3(pl.threads), pl.lds_bytes, stream, p); break;
-    case 4: hipLaunchKernelGGL(layout_tiles_kernel<4>, dim3(blocks), dim3(pl.threads), pl.lds_bytes, stream, p); break;
-    case 2: hipLaunchKernelGGL(layout_tiles_kernel<2>, dim3(blocks), dim3(pl.threads), pl.lds_bytes, stream, p); break;
-    default: hipLaunchKernelGGL(layout_tiles_kernel<1>, dim3(blocks), dim3(pl.threads), pl.lds_bytes, stream, p); break;
+    case 16: err = launch_tiles<16>(pl, p, blocks, stream); break;
+    case 8: err = launch_tiles<8>(pl, p, blocks, stream); break;
+    case 4: err = launch_tiles<4>(pl, p, blocks, stream); break;
+    case 2: err = launch_tiles<2>(pl, p, blocks, stream); break;
+    default: err = launch_tiles<1>(pl, p, blocks, stream); break;
   }
-  hipError_t err = hipGetLastError();
   if (err != hipSuccess || pl.ntiles == 1) return err;
   hipLaunchKernelGGL(layout_finalize_kernel, dim3(pl.ntiles), dim3(pl.fin_threads), pl.fin_lds_bytes, stream, p);
   return hipGetLastError();

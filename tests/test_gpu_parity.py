@@ -152,6 +152,9 @@ LAYOUT_EDGE = [
     ("k64", 100, 64, 128, 4, 1, 0, 0.0, 0.0, None),
     ("hot_expert", 20000, 2, 8, 4, 1, 0, 0.0, 0.0, 0),
     ("many_tiles", 65536, 8, 256, 8, 1, 0, 0.0, 0.0, None),
+    # more tiles than can be resident at once: the two-kernel path
+    ("too_many_tiles_for_one_launch", 70000, 8, 256, 8, 1, 0, 0.01, 0.0, None),
+    ("padded_multitile", 3000, 8, 64, 8, 1, 200, 0.0, 0.0, None),
 ]
 
 

@@ -213,7 +213,7 @@ def traffic_from(fetch_dir, write_dir):
     w_scale = gib_kib / float(np.median(write["copy"]))
     fb = float(np.median(fetch["combine"])) * f_scale * 1024
     wb = float(np.median(write["combine"])) * w_scale * 1024
-    rec = {"kernel": "combine_kernel<8, NT, NT> on the 8192-token workload", "source_hash": source_hash(),
+    rec = {"kernel": "combine_kernel<8, nt loads, sc1 stores> on the 8192-token workload", "source_hash": source_hash(),
            "fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
            "algorithmic_bytes_per_launch": bytes_combine(wl.WORKLOADS["v3"]),
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),

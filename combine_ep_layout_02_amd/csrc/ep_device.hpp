@@ -25,13 +25,23 @@ constexpr int kBufferWord3 = 0x00020000;
 
 // Cache-policy bits of the buffer instructions' aux operand on gfx94x/gfx950.
 constexpr int kAuxDefault = 0;
-constexpr int kAuxNT = 2;  // non-temporal: stream through, do not keep
+constexpr int kAuxNT = 2;    // nt: non-temporal, stream through
+constexpr int kAuxSC1 = 16;  // sc1: device-scope store
 
-// Receive-buffer traffic above which dispatch / combine switch to
-// non-temporal row accesses.  Small (decode-sized) calls keep their rows in
-// L2 and the 256 MB Infinity Cache; large ones stream, so the written rows do
-// not sit dirty in the caches and the gathered rows do not evict them.
+// Receive-buffer traffic above which dispatch / combine switch to streaming
+// cache policies.  Small (decode-sized) calls keep everything in L2 and the
+// 256 MB Infinity Cache.  Large ones, as measured on MI355X for the
+// 8192-token step:
+//   - dispatch stores its receive rows with nt, so they do not sit dirty in
+//     the caches and get written back during the next kernel;
+//   - combine gathers its rows with nt loads, so they do not evict anything;
+//   - combine stores its output with sc1 while the output fits in half of the
+//     256 MB Infinity Cache (the writes then interleave far less with the
+//     gathered reads at the DRAM: at 8192 tokens the output costs ~36 us with
+//     sc1 vs 46 us with nt beside 137 us of reads), and with nt beyond that
+//     (a 235 MB output thrashes the cache and sc1 loses 5% at 16384 tokens).
 constexpr int64_t kStreamingBytes = (int64_t)64 << 20;
+constexpr int64_t kCacheableOutputBytes = (int64_t)128 << 20;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)num_bytes, kBufferWord3);

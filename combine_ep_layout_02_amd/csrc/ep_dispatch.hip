@@ -240,17 +240,25 @@ void launch_fp8_nc(const Split& s, const RowParams& p, bool streaming, hipStream
 
 }  // namespace
 
-// The instantiation used is the smallest chunk capacity in {2, 4, 8, 16}
-// that holds a wavefront's chunks, so narrow slices carry no dead registers
-// or instructions.
+// The instantiation's chunk capacity equals the (even) chunks per wavefront,
+// so no slice carries dead registers or instructions.
+#define EP_BY_CAPACITY(FN, s, ...)                  \
+  switch (s.cpw) {                                  \
+    case 2: FN<2>(s, __VA_ARGS__); break;           \
+    case 4: FN<4>(s, __VA_ARGS__); break;           \
+    case 6: FN<6>(s, __VA_ARGS__); break;           \
+    case 8: FN<8>(s, __VA_ARGS__); break;           \
+    case 10: FN<10>(s, __VA_ARGS__); break;         \
+    case 12: FN<12>(s, __VA_ARGS__); break;         \
+    case 14: FN<14>(s, __VA_ARGS__); break;         \
+    default: FN<16>(s, __VA_ARGS__); break;         \
+  }
+
 hipError_t launch_dispatch_bf16(const RowParams& p, hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
   const Split s = split_for(p);
   const bool streaming = (int64_t)p.T * p.k * p.H * 2 >= kStreamingBytes;
-  if (s.cpw <= 2) launch_bf16_nc<2>(s, p, streaming, stream);
-  else if (s.cpw <= 4) launch_bf16_nc<4>(s, p, streaming, stream);
-  else if (s.cpw <= 8) launch_bf16_nc<8>(s, p, streaming, stream);
-  else launch_bf16_nc<16>(s, p, streaming, stream);
+  EP_BY_CAPACITY(launch_bf16_nc, s, p, streaming, stream);
   return hipGetLastError();
 }
 
@@ -258,12 +266,11 @@ hipError_t launch_dispatch_fp8(const RowParams& p, hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
   const Split s = split_for(p);
   const bool streaming = (int64_t)p.T * p.k * p.H >= kStreamingBytes;
-  if (s.cpw <= 2) launch_fp8_nc<2>(s, p, streaming, stream);
-  else if (s.cpw <= 4) launch_fp8_nc<4>(s, p, streaming, stream);
-  else if (s.cpw <= 8) launch_fp8_nc<8>(s, p, streaming, stream);
-  else launch_fp8_nc<16>(s, p, streaming, stream);
+  EP_BY_CAPACITY(launch_fp8_nc, s, p, streaming, stream);
   return hipGetLastError();
 }
+
+#undef EP_BY_CAPACITY
 
 hipError_t launch_check_cvt_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
   if (n == 0) return hipSuccess;

@@ -35,11 +35,23 @@ __device__ __forceinline__ int aligned_count(int c, int A) { return ((c + A - 1)
 
 __device__ __forceinline__ int udiv(uint32_t n, uint32_t magic) { return (int)__umulhi(n, magic); }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP: four
+// row_shr steps scan each 16-lane row, then two row broadcasts carry row
+// totals into the rows above (lanes without a source add 0).
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
 // Exclusive scan over experts of the (aligned) counts in cnt[0..E): offs[e]
 // for e <= E.  Padded layouts use e*C directly.  Each thread takes a run of
-// experts, wavefronts scan their runs with shuffles, and every thread adds
-// the totals of the wavefronts before it (no serial step).  Ends with a
-// barrier.
+// experts, wavefronts scan their runs with DPP, and every thread adds the
+// totals of the wavefronts before it (no serial step).  Ends with a barrier.
 __device__ void scan_offsets(const int* cnt, int* offs, int E, int A, int C, int* s_part) {
   const int tid = threadIdx.x, nthr = blockDim.x;
   if (C > 0) {
@@ -50,24 +62,28 @@ __device__ void scan_offsets(const int* cnt, int* offs, int E, int A, int C, int
   const int per = (E + nthr - 1) / nthr;
   const int lo = min(E, tid * per), hi = min(E, lo + per);
   int sum = 0;
-  for (int e = lo; e < hi; ++e) sum += aligned_count(cnt[e], A);
-  const int lane = tid & 63, wv = tid >> 6, nw = (nthr + 63) >> 6;
-  int incl = sum;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
+  if (A == 1) {
+    for (int e = lo; e < hi; ++e) sum += cnt[e];
+  } else {
+    for (int e = lo; e < hi; ++e) sum += aligned_count(cnt[e], A);
   }
+  const int lane = tid & 63, wv = tid >> 6, nw = (nthr + 63) >> 6;
+  const int incl = wave_inclusive_scan(sum);
   if (lane == 63) s_part[wv] = incl;
   __syncthreads();
   int before = 0, total = 0;
-  for (int i = 0; i < nw; ++i) {
-    const int v = s_part[i];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int v = i < nw ? s_part[i] : 0;
     before += i < wv ? v : 0;
     total += v;
   }
   int run = before + incl - sum;
-  for (int e = lo; e < hi; ++e) { offs[e] = run; run += aligned_count(cnt[e], A); }
+  if (A == 1) {
+    for (int e = lo; e < hi; ++e) { offs[e] = run; run += cnt[e]; }
+  } else {
+    for (int e = lo; e < hi; ++e) { offs[e] = run; run += aligned_count(cnt[e], A); }
+  }
   if (tid == 0) offs[E] = total;
   __syncthreads();
 }
@@ -157,6 +173,8 @@ __device__ void tile_pass(const LayoutParams& p, const TileLds<W>& L, int tile, 
   const int64_t g0 = (int64_t)t0 * k;
   const bool small_r = R <= 64;
 
+  // the pair's id is loaded first; its latency overlaps the LDS set-up
+  const int v = tid < np ? p.idx[g0 + tid] : -1;
   for (int i = tid; i < W * E; i += nthr) L.masks[i] = 0;
   L.tokrank[tid] = 0;
   for (int i = tid; i < E; i += nthr) L.rank_of[i] = udiv((uint32_t)i, p.magic_per);
@@ -167,7 +185,6 @@ __device__ void tile_pass(const LayoutParams& p, const TileLds<W>& L, int tile, 
   int e = -1;
   bool bad = false;
   if (tid < np) {
-    const int v = p.idx[g0 + tid];
     if (v >= 0 && v < E) e = v;
     else bad = (v != -1);
   }
@@ -260,16 +277,18 @@ __device__ void reduce_tiles(const LayoutParams& p, int tile, int G, int* part_t
 }
 
 // Block 0 only: rank counts and invalid ids summed over tiles (coalesced
-// sweeps, LDS atomics); rank_tot must be zero.  Ends with a barrier.
-__device__ void reduce_ranks(const LayoutParams& p, int* rank_tot, int* s_bad) {
+// sweeps, LDS atomics); rank_tot must be zero.  Entries tid of both arrays
+// arrive preloaded in rank0 / bad0.  Ends with a barrier.
+__device__ void reduce_ranks(const LayoutParams& p, int* rank_tot, int* s_bad, int rank0, int bad0) {
   const int R = p.R, ntiles = p.ntiles;
   const int tid = threadIdx.x, nthr = blockDim.x;
-  for (int i = tid; i < ntiles * R; i += nthr) {
+  if (rank0) atomicAdd(&rank_tot[tid - udiv((uint32_t)tid, p.magic_R) * R], rank0);
+  for (int i = tid + nthr; i < ntiles * R; i += nthr) {
     const int v = p.ws_rank[i];
     if (v) atomicAdd(&rank_tot[i - udiv((uint32_t)i, p.magic_R) * R], v);
   }
-  int bad = 0;
-  for (int t = tid; t < ntiles; t += nthr) bad += p.ws_bad[t];
+  int bad = bad0;
+  for (int t = tid + nthr; t < ntiles; t += nthr) bad += p.ws_bad[t];
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) bad += __shfl_xor(bad, d, 64);
   if ((tid & 63) == 0 && bad) atomicAdd(s_bad, bad);
@@ -345,26 +364,35 @@ __global__ __launch_bounds__(1024) void layout_finalize_kernel(LayoutParams p) {
   const FinLds F(smem, p.G, E);
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int tile = blockIdx.x;
+  // this thread's pair (a tile has at most 1024 pairs, one per thread),
+  // loaded up front so its latency overlaps the reductions
+  const int t0 = tile * p.TT;
+  const int np = max(0, min(p.TT, p.T - t0)) * p.k;
+  const int64_t g0 = (int64_t)t0 * p.k;
+  int v = -1, local = 0;
+  if (tid < np) {
+    v = p.idx[g0 + tid];
+    local = p.slot[g0 + tid];
+  }
+  // block 0 also sums the per-tile rank counts and invalid ids; its first
+  // share of them is loaded here too
+  const bool lead = tile == 0;
+  const int nrank = p.ntiles * R;
+  const int rank0 = lead && tid < nrank ? p.ws_rank[tid] : 0;
+  const int bad0 = lead && tid < p.ntiles ? p.ws_bad[tid] : 0;
   for (int r = tid; r < R; r += nthr) F.rank_tot[r] = 0;
   if (tid == 0) s_bad = 0;
   reduce_tiles(p, tile, p.G, F.part_tot, F.part_pre, F.tot, F.pre);
-  if (tile == 0) reduce_ranks(p, F.rank_tot, &s_bad);
+  if (lead) reduce_ranks(p, F.rank_tot, &s_bad, rank0, bad0);
   if (tile == 0 && tid == 0 && p.diag) { p.diag[0] = s_bad; p.diag[1] = 0; }
   scan_offsets(F.tot, F.offs, E, p.A, p.C, s_part);  // barrier: diag[1] is zero before the adds
 
-  // this tile's slots
-  {
-    const int t0 = tile * p.TT;
-    const int np = max(0, min(p.TT, p.T - t0)) * p.k;
-    const int64_t g0 = (int64_t)t0 * p.k;
-    for (int i = tid; i < np; i += nthr) {
-      const int v = p.idx[g0 + i];
-      if (!(v >= 0 && v < E)) continue;  // slot already -1
-      int s = slot_of(p, v, F.pre[v] + p.slot[g0 + i], F.offs);
-      if ((int64_t)s >= p.rows) s = -1;  // cannot happen; keeps every write in bounds
-      p.slot[g0 + i] = s;
-      if (s >= 0 && p.src_pair) p.src_pair[s] = (int)(g0 + i);
-    }
+  // this tile's slots (an invalid id's slot is already -1)
+  if (tid < np && v >= 0 && v < E) {
+    int s = slot_of(p, v, F.pre[v] + local, F.offs);
+    if ((int64_t)s >= p.rows) s = -1;  // cannot happen; keeps every write in bounds
+    p.slot[g0 + tid] = s;
+    if (s >= 0 && p.src_pair) p.src_pair[s] = (int)(g0 + tid);
   }
   if (tile == 0) write_outputs(p, F.tot, F.offs, F.rank_tot);
   const int nw = nthr >> 6;

@@ -10,9 +10,13 @@ is algorithmic bytes per step (layout + dispatch + combine, counted as the
 method must move them) times K over the wall time of K steps.
 
 Also reported: per-stage kernel times from HIP events recorded around each
-call in a second timed loop, the roofline of the dominant kernel (combine,
-HBM-bound), the decode-shaped workload's microseconds per call, and the CPU
-oracle timed on this host (one thread) on the same workload.
+call in a second timed loop (mean, median, p10, p90), the roofline of the
+dominant kernel (combine, HBM-bound), the same step "cold" (each step after
+reading a 1 GiB buffer, so no cache holds its data), the decode-shaped
+workload's microseconds per call, warm and cold step times of the tiny, mid
+and 16K-token skewed workloads, a plain 1 GiB copy as the practical
+bandwidth ceiling, and the CPU oracle timed on this host (one thread) on the
+same workload.
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 
@@ -21,8 +25,8 @@ runs of this script (FETCH_SIZE, then WRITE_SIZE) with --calibration-copy,
 which adds a plain 1 GiB device copy whose true byte counts scale the
 counters:
 
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d F -- python3 bench.py --steps 3 --warmup 1 --no-decode --no-cpu-baseline --calibration-copy
-    rocprofv3 --pmc WRITE_SIZE --output-format csv -d W -- python3 bench.py --steps 3 --warmup 1 --no-decode --no-cpu-baseline --calibration-copy
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d F -- python3 bench.py --steps 3 --warmup 1 --no-decode --no-configs --no-cpu-baseline --calibration-copy
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d W -- python3 bench.py --steps 3 --warmup 1 --no-decode --no-configs --no-cpu-baseline --calibration-copy
     python3 bench.py --traffic-from F W
 
 The last command writes profiles/combine_v3_traffic.json, stamped with a hash
@@ -99,11 +103,12 @@ class Step:
         self.dtype = ep.EP_FP8_E4M3 if fp8 else ep.EP_BF16
         self.recv_x, self.recv_scale = ep.alloc_recv(self.shape, self.dtype, dev)
         self.out = torch.empty_like(self.x)
-        # argument checks once; the timed loop only launches
-        self.layout = self.lay.prepare(self.idx)
+        # argument checks and the stream lookup once; the timed loop only launches
+        stream = torch.cuda.current_stream(dev)
+        self.layout = self.lay.prepare(self.idx, stream)
         self.dispatch = ep.prepare_dispatch(self.shape, self.x, self.lay.slot, self.dtype, self.recv_x,
-                                            self.recv_scale)
-        self.combine = ep.prepare_combine(self.shape, self.y, self.lay.slot, self.wts, self.out)
+                                            self.recv_scale, stream)
+        self.combine = ep.prepare_combine(self.shape, self.y, self.lay.slot, self.wts, self.out, stream)
 
     def run(self):
         self.layout()
@@ -131,11 +136,14 @@ def time_steps(step, steps, warmup):
     return start.elapsed_time(end), time.perf_counter() - t0
 
 
-def time_stages(step, steps):
-    """Per-stage kernel time: HIP events around each call, on the launch stream."""
+def time_stages(step, steps, flush=None):
+    """Per-stage kernel time: HIP events around each call, on the launch stream.
+    With `flush`, it runs before each step, outside the events."""
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     for e in ev:
+        if flush is not None:
+            flush()
         e[0].record()
         step.layout()
         e[1].record()
@@ -145,6 +153,58 @@ def time_stages(step, steps):
         e[3].record()
     torch.cuda.synchronize()
     return np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])  # ms
+
+
+class ReadFlush:
+    """Reads a 1 GiB buffer (a sum into one int64): afterwards the 256 MB
+    Infinity Cache and the L2s hold clean lines of that buffer, none of the
+    step's data, and there is no dirty data whose write-back the next step
+    would pay for (as there would be after writing the buffer)."""
+
+    def __init__(self, dev):
+        self.buf = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+        self.sink = torch.empty((), dtype=torch.int64, device=dev)
+
+    def __call__(self):
+        self.sink.copy_(self.buf.sum(dtype=torch.int64))
+
+
+def time_cold(step, reps, flush):
+    """Whole-step time after a cache flush: two events around each step."""
+    ms = []
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step.run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    return np.array(ms)
+
+
+def pct(a, q):
+    return round(float(np.percentile(a, q)) * 1e3, 2)
+
+
+def spread_us(a):
+    """median, p10 and p90 of times in ms, as microseconds."""
+    return {"median": pct(a, 50), "p10": pct(a, 10), "p90": pct(a, 90)}
+
+
+def summarize_config(w, fp8, dev, steps, flush):
+    """Warm (back-to-back) and cold (flushed) step time of one more workload."""
+    step = Step(w, dev, fp8=fp8)
+    total_ms, _ = time_steps(step, steps, 5)
+    cold = time_cold(step, 10, flush)
+    nbytes = step.bytes
+    warm_us = total_ms / steps * 1e3
+    cold_us = float(np.median(cold)) * 1e3
+    return {"dispatch": "fp8_e4m3" if fp8 else "bf16", "tokens": w.num_tokens, "hidden": w.hidden,
+            "experts": w.num_experts, "topk": w.num_topk, "capacity": w.capacity, "bytes_per_step": nbytes,
+            "warm_us": round(warm_us, 2), "warm_GBps": round(nbytes / warm_us / 1e3, 1),
+            "cold_us": round(cold_us, 2), "cold_GBps": round(nbytes / cold_us / 1e3, 1)}
 
 
 def source_hash():
@@ -248,6 +308,8 @@ def main():
     ap.add_argument("--workload", default="v3", choices=["v3", "skew"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the tiny, mid and 16K-token skewed workloads")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="counter runs: keep the 1 GiB calibration copy to 3 launches")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -275,6 +337,11 @@ def main():
     value = step.bytes * args.steps / (total_ms / 1e3) / 1e9
     stage = time_stages(step, args.steps)
     lay_ms, disp_ms, comb_ms = stage.mean(axis=0)
+    log("[bench] cold steps (1 GiB read before each)")
+    flush = ReadFlush(dev)
+    cold_step = time_cold(step, 20, flush)
+    cold_stage = time_stages(step, 20, flush)
+    cold_us = float(np.median(cold_step)) * 1e3
 
     dec = None
     if not args.no_decode:
@@ -292,6 +359,17 @@ def main():
                        "layout; mean over 500 back-to-back calls (inputs stay in the 256 MB Infinity Cache); "
                        "stage times are medians with events around each kernel"}
         del dstep
+
+    configs = None
+    if not args.no_configs:
+        configs = {}
+        others = [("tiny", False), ("tiny", True), ("mid", False),
+                  ("skew" if w.name != "skew" else "v3", True)]
+        for name, fp8 in others:
+            log(f"[bench] {name} {'fp8' if fp8 else 'bf16'}")
+            configs[f"{name}_{'fp8' if fp8 else 'bf16'}"] = summarize_config(wl.WORKLOADS[name], fp8, dev, 20, flush)
+            torch.cuda.empty_cache()
+    del flush
 
     copy_gbps = calibration_copy(dev, reps=3 if args.calibration_copy else 5)
     cb = None if args.no_cpu_baseline else cpu_baseline(step)
@@ -323,12 +401,20 @@ def main():
                       "combine": round(float(comb_ms) * 1e3, 2)},
         "stage_GBps": {"dispatch": round(bytes_dispatch(w, True) / (disp_ms / 1e3) / 1e9, 1),
                        "combine": round(achieved, 1)},
+        "stages_spread_us": {n: spread_us(stage[:, i]) for i, n in enumerate(("layout", "dispatch", "combine"))},
+        "cold": {"step_us": spread_us(cold_step), "GBps": round(step.bytes / cold_us / 1e3, 1),
+                 "pct_of_hbm_peak": round(100 * step.bytes / cold_us / 1e3 / HBM_PEAK_GBS, 2),
+                 "stages_us": {n: spread_us(cold_stage[:, i])
+                               for i, n in enumerate(("layout", "dispatch", "combine"))},
+                 "note": "20 steps, each after reading a 1 GiB buffer, so that neither the Infinity Cache nor "
+                         "the L2s hold any of the step's data"},
         "roofline": {"kernel": "combine", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": comb_bytes},
         "copy_ceiling": {"GBps": round(copy_gbps, 1), "kernel": "torch bitwise_not, 1 GiB in + 1 GiB out",
                          "step_frac_of_copy": round(value / copy_gbps, 4)},
         "decode": dec,
+        "configs": configs,
         "cpu_baseline": cb,
         "wall_s_timed": round(wall, 4),
     }

@@ -238,20 +238,28 @@ def ep_check_cvt_bf16(inp, out, stream=None) -> None:
 # ---------------------------------------------------------------------------
 
 class Prepared:
-    """One entry point bound to fixed, already checked arguments."""
-    __slots__ = ("name", "_fn", "_args", "_keep")
+    """One entry point bound to fixed, already checked arguments.
 
-    def __init__(self, name, fn, args, keep):
+    With `stream` given at prepare time the handle is resolved once and every
+    call without a stream of its own launches there, which saves looking up
+    torch's current stream on each call (a few microseconds per step of a
+    decode loop).  Without it each call launches on torch's current stream.
+    """
+    __slots__ = ("name", "_fn", "_args", "_keep", "_bound")
+
+    def __init__(self, name, fn, args, keep, stream=None):
         self.name, self._fn, self._args, self._keep = name, fn, args, keep
+        self._bound = None if stream is None else _stream(stream)
 
     def __call__(self, stream=None) -> None:
-        status = self._fn(*self._args, _stream(stream))
+        s = _stream(stream) if stream is not None or self._bound is None else self._bound
+        status = self._fn(*self._args, s)
         if status != EP_OK:
             _check(self.name, status)
 
 
 def prepare_layout(shape: EpShape, topk_idx, expert_count, expert_offset, rank_count, rank_offset, slot,
-                   src_pair=None, diag=None, workspace=None) -> Prepared:
+                   src_pair=None, diag=None, workspace=None, stream=None) -> Prepared:
     T, k, E, R = shape.num_tokens, shape.num_topk, shape.num_experts, shape.num_ranks
     rows, ws_bytes = shape.recv_rows, shape.workspace_bytes
     i32 = torch.int32
@@ -267,10 +275,10 @@ def prepare_layout(shape: EpShape, topk_idx, expert_count, expert_offset, rank_c
     if nbytes < ws_bytes:
         raise ValueError(f"workspace has {nbytes} bytes, needs {ws_bytes}")
     keep = (topk_idx, expert_count, expert_offset, rank_count, rank_offset, slot, src_pair, diag, workspace)
-    return Prepared("ep_layout", lib().ep_layout, (shape.c_ref, *args, nbytes), keep)
+    return Prepared("ep_layout", lib().ep_layout, (shape.c_ref, *args, nbytes), keep, stream)
 
 
-def prepare_dispatch(shape: EpShape, x, slot, recv_dtype: int, recv_x, recv_scale=None) -> Prepared:
+def prepare_dispatch(shape: EpShape, x, slot, recv_dtype: int, recv_x, recv_scale=None, stream=None) -> Prepared:
     T, H, k = shape.num_tokens, shape.hidden, shape.num_topk
     rows = shape.recv_rows
     if recv_dtype == EP_BF16:
@@ -282,17 +290,17 @@ def prepare_dispatch(shape: EpShape, x, slot, recv_dtype: int, recv_x, recv_scal
         raise ValueError(f"unknown recv_dtype {recv_dtype}")
     args = (shape.c_ref, _ptr(x, "x", _BF16_LIKE, T * H, optional=T == 0),
             _ptr(slot, "slot", torch.int32, T * k, optional=T == 0), int(recv_dtype), rx, rs)
-    return Prepared("ep_dispatch", lib().ep_dispatch, args, (x, slot, recv_x, recv_scale))
+    return Prepared("ep_dispatch", lib().ep_dispatch, args, (x, slot, recv_x, recv_scale), stream)
 
 
-def prepare_combine(shape: EpShape, y, slot, topk_weights, out) -> Prepared:
+def prepare_combine(shape: EpShape, y, slot, topk_weights, out, stream=None) -> Prepared:
     T, H, k = shape.num_tokens, shape.hidden, shape.num_topk
     rows = shape.recv_rows
     args = (shape.c_ref, _ptr(y, "y", _BF16_LIKE, rows * H, optional=T == 0),
             _ptr(slot, "slot", torch.int32, T * k, optional=T == 0),
             _ptr(topk_weights, "topk_weights", torch.float32, T * k, optional=T == 0),
             _ptr(out, "out", _BF16_LIKE, T * H, optional=T == 0))
-    return Prepared("ep_combine", lib().ep_combine, args, (y, slot, topk_weights, out))
+    return Prepared("ep_combine", lib().ep_combine, args, (y, slot, topk_weights, out), stream)
 
 
 # ---------------------------------------------------------------------------
@@ -328,9 +336,9 @@ class LayoutBuffers:
                   self.rank_offset, self.slot, self.src_pair, self.diag, self.workspace, stream)
         return self
 
-    def prepare(self, topk_idx: torch.Tensor) -> Prepared:
+    def prepare(self, topk_idx: torch.Tensor, stream=None) -> Prepared:
         return prepare_layout(self.shape, topk_idx, self.expert_count, self.expert_offset, self.rank_count,
-                              self.rank_offset, self.slot, self.src_pair, self.diag, self.workspace)
+                              self.rank_offset, self.slot, self.src_pair, self.diag, self.workspace, stream)
 
 
 def alloc_recv(shape: EpShape, recv_dtype: int, device="cuda"):

@@ -60,6 +60,8 @@ def lib():
         L.oracle_dispatch_bf16.argtypes = [i64, i64, i64, vp, vp, vp]
         L.oracle_dispatch_fp8.argtypes = [i64, i64, i64, vp, vp, vp, vp]
         L.oracle_combine.argtypes = [i64, i64, i64, vp, vp, vp, vp]
+        L.oracle_dispatch_backward.argtypes = [i64, i64, i64, vp, vp, vp]
+        L.oracle_combine_backward.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -158,3 +160,30 @@ def combine(y: np.ndarray, slot: np.ndarray, weights: np.ndarray) -> np.ndarray:
     out = np.zeros((T, H), np.uint16)
     lib().oracle_combine(T, H, k, _p(y), _p(slot), _p(w), _p(out))
     return out
+
+
+def dispatch_backward(grad_recv: np.ndarray, slot: np.ndarray) -> np.ndarray:
+    """Gradient of x given the gradient of the dispatched rows (BF16 bits)."""
+    g = _c(grad_recv, np.uint16)
+    slot = _c(slot, np.int32)
+    T, k = slot.shape
+    H = g.shape[1]
+    out = np.zeros((T, H), np.uint16)
+    lib().oracle_dispatch_backward(T, H, k, _p(g), _p(slot), _p(out))
+    return out
+
+
+def combine_backward(grad_out: np.ndarray, y: np.ndarray, slot: np.ndarray, weights: np.ndarray,
+                     grad_y_init: Optional[np.ndarray] = None):
+    """Gradients of y (BF16 bits, [rows, H]; rows no pair maps to keep
+    grad_y_init, zeros by default) and of the weights (float64 [T, k])."""
+    g = _c(grad_out, np.uint16)
+    y = _c(y, np.uint16)
+    slot = _c(slot, np.int32)
+    w = _c(weights, np.float32)
+    T, k = slot.shape
+    H = g.shape[1]
+    gy = np.zeros(y.shape, np.uint16) if grad_y_init is None else np.array(grad_y_init, np.uint16)
+    gw = np.zeros((T, k), np.float64)
+    lib().oracle_combine_backward(T, H, k, _p(g), _p(y), _p(slot), _p(w), _p(gy), _p(gw))
+    return gy, gw

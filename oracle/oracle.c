@@ -40,7 +40,13 @@
  *   R8  one fp32 scale per (row, 128-column block):
  *       s = max(amax, 1e-4) / 448, code = E4M3(x / s), all in fp32;
  *   R9  combine: acc = +0; for j ascending over valid slots
- *       acc = fmaf(w[t,j], y[slot[t,j], h], acc); out = BF16_RNE(acc).
+ *       acc = fmaf(w[t,j], y[slot[t,j], h], acc); out = BF16_RNE(acc);
+ *   R10 dispatch backward: acc = +0; for j ascending over valid slots
+ *       acc = acc + grad_recv[slot[t,j], h] (fp32); grad_x = BF16_RNE(acc);
+ *   R11 combine backward: grad_y[slot[t,j], h] = BF16_RNE(w[t,j] * g[t,h])
+ *       with the product rounded to fp32 first; grad_w[t,j] = the exact dot
+ *       product of g[t] and y[slot[t,j]] (returned in double); the BF16
+ *       rounding of the forward output passes the gradient through as is.
  *
  * Build: gcc -O2 -std=c99 -ffp-contract=off -fPIC -shared oracle.c -lm
  * (no fast-math: every float operation below is one IEEE-754 binary32
@@ -339,6 +345,85 @@ void oracle_combine(int64_t T, int64_t H, int64_t k,
                 acc = fmaf(w[t * k + j], bf16_to_f32(y[(int64_t)s * H + h]), acc);
             }
             out[t * H + h] = oracle_bf16_rne(acc);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Backward pair                                                       */
+/* ------------------------------------------------------------------ */
+/*
+ * DeepEP runs the backward of dispatch as a combine and the backward of
+ * combine as a dispatch, over the same routing handle (GeekNews "DeepSeek
+ * publica DeepEP ...", section "Patrones de uso en entrenamiento, prefill y
+ * decoding"; DeepEP documentation, item 10, "Backward Pass").  The two
+ * functions below are the gradients of the forward definitions above.
+ */
+
+/*
+ * Dispatch backward (R10).  Forward, recv[slot[t,j]] = x[t] for each valid
+ * pair, so the gradient of x[t] is the sum of the gradients of its received
+ * copies.  Copies that were masked or dropped (slot -1) carry none.  The sum
+ * runs in fp32 from +0 in ascending j, rounded once to BF16; it is the
+ * combine of R9 with every weight 1 (fmaf(1, v, acc) == acc + v).
+ *
+ * grad_recv [rows, H] BF16 bits; slot [T, k]; grad_x [T, H] BF16 bits.
+ */
+void oracle_dispatch_backward(int64_t T, int64_t H, int64_t k,
+                              const uint16_t *grad_recv, const int32_t *slot,
+                              uint16_t *grad_x)
+{
+    int64_t t, h, j;
+    for (t = 0; t < T; ++t) {
+        for (h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (j = 0; j < k; ++j) {
+                int32_t s = slot[t * k + j];
+                if (s < 0) continue;
+                acc = acc + bf16_to_f32(grad_recv[(int64_t)s * H + h]);
+            }
+            grad_x[t * H + h] = oracle_bf16_rne(acc);
+        }
+    }
+}
+
+/*
+ * Combine backward (R11).  Forward, out[t] = sum over valid j of
+ * w[t,j] * y[slot[t,j]], so for the gradient g = d loss / d out:
+ *   d/dy[slot[t,j]] = w[t,j] * g[t]      (a dispatch of g, scaled per copy)
+ *   d/dw[t,j]       = <g[t], y[slot[t,j]]>
+ * grad_y rows: the fp32 product w * g (one IEEE multiply, nearest-even),
+ * then BF16 nearest-even.  Rows that no valid pair maps to are not written.
+ * grad_w: every product of two BF16 values is exact in double (8 + 8
+ * significant bits), and the double sum over h carries a relative error of
+ * at most H * 2^-53, so grad_w here is the exact dot product for all
+ * practical purposes; the GPU's fp32 sum is compared to it within the
+ * fp32 summation bound.  A masked or dropped pair gets grad_w = 0.
+ *
+ * g [T, H], y [rows, H] BF16 bits; slot, w [T, k]; grad_y [rows, H] BF16
+ * bits (only valid rows written); grad_w [T, k] double.
+ */
+void oracle_combine_backward(int64_t T, int64_t H, int64_t k,
+                             const uint16_t *g, const uint16_t *y,
+                             const int32_t *slot, const float *w,
+                             uint16_t *grad_y, double *grad_w)
+{
+    int64_t t, h, j;
+    for (t = 0; t < T; ++t) {
+        for (j = 0; j < k; ++j) {
+            int32_t s = slot[t * k + j];
+            double dot = 0.0;
+            if (s < 0) {
+                grad_w[t * k + j] = 0.0;
+                continue;
+            }
+            for (h = 0; h < H; ++h) {
+                float gv = bf16_to_f32(g[t * H + h]);
+                float prod = w[t * k + j] * gv;
+                grad_y[(int64_t)s * H + h] = oracle_bf16_rne(prod);
+                dot += (double)gv * (double)bf16_to_f32(y[(int64_t)s * H + h]);
+            }
+            grad_w[t * k + j] = dot;
         }
     }
 }

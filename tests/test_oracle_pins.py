@@ -380,6 +380,168 @@ def test_combine_skips_masked_slots():
 
 
 # --------------------------------------------------------------------------
+# backward pair
+# --------------------------------------------------------------------------
+
+def _bits(rows):
+    return [[int(b, 16) for b in r] for r in rows]
+
+
+def test_dispatch_backward_hand_fixture():
+    g = _golden("backward_hand.json")
+    d = g["dispatch_backward"]
+    gx = oracle.dispatch_backward(wl.f32_to_bf16_bits(np.array(d["grad_recv"], np.float32)),
+                                  np.array(g["slot"], np.int32))
+    assert gx.tolist() == _bits(d["grad_x_bits"])
+
+
+def test_combine_backward_hand_fixture():
+    g = _golden("backward_hand.json")
+    c = g["combine_backward"]
+    sentinel = np.full((g["rows"], g["H"]), 0x7E7E, np.uint16)
+    gy, gw = oracle.combine_backward(wl.f32_to_bf16_bits(np.array(c["grad_out"], np.float32)),
+                                     wl.f32_to_bf16_bits(np.array(c["y"], np.float32)),
+                                     np.array(g["slot"], np.int32), np.array(c["weights"], np.float32),
+                                     sentinel)
+    assert gy.tolist() == _bits(c["grad_y_bits"])
+    assert gw.tolist() == c["grad_w"]
+
+
+def _small_int_bf16(rng, shape, lo=-3, hi=3):
+    return wl.f32_to_bf16_bits(rng.integers(lo, hi + 1, size=shape).astype(np.float32))
+
+
+def _exact_case(seed, T, H, k, E, mask_frac=0.0):
+    """Random routing with small-integer activations and weights in {0.5, 1}:
+    every sum and product below is exact in fp32 and in BF16."""
+    rng = np.random.default_rng(seed)
+    idx = _random_idx(rng, T, k, E, mask_frac=mask_frac)
+    lay = oracle.layout(idx, E, 1)
+    rows = oracle.recv_rows(T, k, E)
+    wts = rng.choice(np.array([0.5, 1.0], np.float32), size=(T, k))
+    return rng, lay, rows, wts
+
+
+@pytest.mark.parametrize("seed,mask", [(0, 0.0), (1, 0.2)])
+def test_dispatch_backward_is_adjoint_of_dispatch(seed, mask):
+    """<dispatch(x), G> == <x, dispatch_backward(G)> exactly (integer data)."""
+    T, H, k, E = 40, 48, 4, 16
+    rng, lay, rows, _ = _exact_case(seed, T, H, k, E, mask)
+    x = _small_int_bf16(rng, (T, H))
+    G = _small_int_bf16(rng, (rows, H))
+    rx = wl.bf16_bits_to_f32(oracle.dispatch_bf16(x, lay.slot, rows)).astype(np.float64)
+    gx = wl.bf16_bits_to_f32(oracle.dispatch_backward(G, lay.slot)).astype(np.float64)
+    Gf = wl.bf16_bits_to_f32(G).astype(np.float64)
+    xf = wl.bf16_bits_to_f32(x).astype(np.float64)
+    assert (rx * Gf).sum() == (xf * gx).sum()
+    # and per token: the gradient of x[t] is the sum over its valid copies
+    valid = lay.slot >= 0
+    want = np.stack([Gf[lay.slot[t][valid[t]]].sum(0) for t in range(T)])
+    assert np.array_equal(gx, want)
+
+
+@pytest.mark.parametrize("seed,mask", [(2, 0.0), (3, 0.25)])
+def test_combine_backward_grad_y_is_adjoint_of_combine(seed, mask):
+    """<combine(y, w), g> == <y, grad_y> exactly (integer data, w in {0.5, 1})."""
+    T, H, k, E = 40, 48, 4, 16
+    rng, lay, rows, wts = _exact_case(seed, T, H, k, E, mask)
+    y = _small_int_bf16(rng, (rows, H))
+    g = _small_int_bf16(rng, (T, H))
+    out = wl.bf16_bits_to_f32(oracle.combine(y, lay.slot, wts)).astype(np.float64)
+    gy, _ = oracle.combine_backward(g, y, lay.slot, wts)
+    lhs = (out * wl.bf16_bits_to_f32(g)).sum()
+    rhs = (wl.bf16_bits_to_f32(y).astype(np.float64) * wl.bf16_bits_to_f32(gy)).sum()
+    assert lhs == rhs
+
+
+@pytest.mark.parametrize("seed,mask", [(4, 0.0), (5, 0.25)])
+def test_combine_backward_grad_w_is_finite_difference_of_combine(seed, mask):
+    """combine is linear in w: <g, combine(w + e_tj)> - <g, combine(w)> = grad_w[t, j]
+    exactly (integer data), for every pair, one j per token at a time."""
+    T, H, k, E = 40, 48, 4, 16
+    rng, lay, rows, wts = _exact_case(seed, T, H, k, E, mask)
+    y = _small_int_bf16(rng, (rows, H))
+    g = _small_int_bf16(rng, (T, H))
+    gf = wl.bf16_bits_to_f32(g).astype(np.float64)
+    base = (wl.bf16_bits_to_f32(oracle.combine(y, lay.slot, wts)) * gf).sum(1)
+    _, gw = oracle.combine_backward(g, y, lay.slot, wts)
+    for j in range(k):
+        w2 = wts.copy()
+        w2[:, j] += 1.0
+        bumped = (wl.bf16_bits_to_f32(oracle.combine(y, lay.slot, w2)) * gf).sum(1)
+        assert np.array_equal(bumped - base, gw[:, j])
+    assert (gw[lay.slot < 0] == 0).all()
+
+
+def test_combine_backward_grad_y_matches_torch_product_and_cast():
+    """Non-trivial weights: grad_y = BF16_RNE(fp32(w * g)) as torch computes it on the CPU."""
+    T, H, k, E = 64, 64, 6, 32
+    rng = np.random.default_rng(6)
+    idx = _random_idx(rng, T, k, E)
+    lay = oracle.layout(idx, E, 4)
+    rows = oracle.recv_rows(T, k, E)
+    wts = rng.random((T, k)).astype(np.float32)
+    g = wl.normal_bf16(6, 0, T, H)
+    y = wl.normal_bf16(6, 2, rows, H)
+    gy, _ = oracle.combine_backward(g, y, lay.slot, wts)
+    gt = torch.from_numpy(wl.bf16_bits_to_f32(g))
+    for t in range(T):
+        for j in range(k):
+            want = (torch.tensor(wts[t, j]) * gt[t]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            assert np.array_equal(gy[lay.slot[t, j]], want)
+
+
+def test_combine_backward_grad_w_matches_float64_dot():
+    """grad_w against numpy's float64 dot of the decoded rows, at a real row width."""
+    T, H, k, E = 16, 7168, 8, 64
+    rng = np.random.default_rng(7)
+    lay = oracle.layout(_random_idx(rng, T, k, E), E, 8)
+    rows = oracle.recv_rows(T, k, E)
+    g = wl.normal_bf16(7, 0, T, H)
+    y = wl.normal_bf16(7, 2, rows, H)
+    _, gw = oracle.combine_backward(g, y, lay.slot, rng.random((T, k)).astype(np.float32))
+    gf = wl.bf16_bits_to_f32(g).astype(np.float64)
+    yf = wl.bf16_bits_to_f32(y).astype(np.float64)
+    want = np.einsum("th,tjh->tj", gf, yf[lay.slot])
+    mag = np.einsum("th,tjh->tj", np.abs(gf), np.abs(yf[lay.slot]))
+    assert (np.abs(gw - want) <= 2 * H * 2.0 ** -53 * mag).all()
+
+
+def test_combine_backward_leaves_unmapped_rows():
+    """Padded layout with a drop: rows that no valid pair maps to keep their contents."""
+    idx = np.array([[0, 1], [0, 2], [0, 1]], np.int32)  # expert 0 gets 3 tokens, capacity 2
+    lay = oracle.layout(idx, 4, 2, 1, 2)
+    assert lay.slot[2, 0] == -1 and lay.diag[1] == 1
+    rows = 8
+    g = wl.normal_bf16(8, 0, 3, 16)
+    y = wl.normal_bf16(8, 2, rows, 16)
+    init = np.full((rows, 16), 0x1234, np.uint16)
+    gy, gw = oracle.combine_backward(g, y, lay.slot, np.full((3, 2), 0.5, np.float32), init)
+    used = set(lay.slot[lay.slot >= 0].tolist())
+    for r in range(rows):
+        assert (gy[r] == 0x1234).all() == (r not in used)
+    assert gw[2, 0] == 0.0
+    gx = oracle.dispatch_backward(y, lay.slot)
+    # the dropped copy of token 2 contributes nothing: grad_x[2] = y[slot[2, 1]]
+    assert np.array_equal(gx[2], y[lay.slot[2, 1]])
+
+
+def test_dispatch_backward_k1_is_gather_and_within_bound():
+    rng = np.random.default_rng(9)
+    G = wl.normal_bf16(9, 2, 50, 64)
+    slot = rng.permutation(50)[:40].astype(np.int32)[:, None]
+    assert np.array_equal(oracle.dispatch_backward(G, slot), G[slot[:, 0]])
+    # k = 8 random rows: within half a BF16 ulp plus the fp32 sum bound of the exact sum
+    T, k = 30, 8
+    slot = np.stack([rng.permutation(50)[:k] for _ in range(T)]).astype(np.int32)
+    gx = wl.bf16_bits_to_f32(oracle.dispatch_backward(G, slot)).astype(np.float64)
+    Gf = wl.bf16_bits_to_f32(G).astype(np.float64)
+    exact = Gf[slot].sum(1)
+    half_ulp = np.ldexp(1.0, np.frexp(np.abs(gx))[1] - 9)
+    assert (np.abs(gx - exact) <= half_ulp + k * 2.0 ** -24 * np.abs(Gf[slot]).sum(1) + 1e-45).all()
+
+
+# --------------------------------------------------------------------------
 # generators
 # --------------------------------------------------------------------------
 

@@ -13,7 +13,8 @@ Also reported: per-stage kernel times from HIP events recorded around each
 call in a second timed loop (mean, median, p10, p90), the roofline of the
 dominant kernel (combine, HBM-bound), the same step "cold" (each step after
 reading a 1 GiB buffer, so no cache holds its data), the decode-shaped
-workload's microseconds per call, warm and cold step times of the tiny, mid
+workload's microseconds per call, the backward pair's kernel times on the
+same handle, warm and cold step times of the tiny, mid
 and 16K-token skewed workloads, a plain 1 GiB copy as the practical
 bandwidth ceiling, and the CPU oracle timed on this host (one thread) on the
 same workload.
@@ -80,6 +81,16 @@ def bytes_dispatch(w, fp8):
 def bytes_combine(w):
     T, H, k = w.num_tokens, w.hidden, w.num_topk
     return 2 * T * k * H + 8 * T * k + 2 * T * H
+
+
+def bytes_dispatch_backward(w):
+    T, H, k = w.num_tokens, w.hidden, w.num_topk
+    return 2 * T * k * H + 4 * T * k + 2 * T * H
+
+
+def bytes_combine_backward(w):
+    T, H, k = w.num_tokens, w.hidden, w.num_topk
+    return 2 * T * H + 4 * T * k * H + 12 * T * k
 
 
 # --------------------------------------------------------------------------
@@ -182,6 +193,41 @@ def time_cold(step, reps, flush):
         torch.cuda.synchronize()
         ms.append(e0.elapsed_time(e1))
     return np.array(ms)
+
+
+def time_backward(step, reps):
+    """The backward pair on the step's handle: dispatch backward of a gradient
+    shaped like the received rows, combine backward of an output gradient
+    (with the gate-weight gradient).  Events around each call."""
+    w, dev = step.w, step.x.device
+    stream = torch.cuda.current_stream(dev)
+    grad_recv = step.y                       # any BF16 [rows, H] buffer serves as the gradient
+    grad_x = torch.empty_like(step.x)
+    grad_out = step.x                        # and any BF16 [T, H] one as the output gradient
+    grad_y = torch.empty_like(step.y)
+    grad_w = torch.empty_like(step.wts)
+    dbw = ep.prepare_dispatch_backward(step.shape, grad_recv, step.lay.slot, grad_x, stream)
+    cbw = ep.prepare_combine_backward(step.shape, grad_out, step.y, step.lay.slot, step.wts, grad_y, grad_w,
+                                      stream)
+    for _ in range(3):
+        dbw()
+        cbw()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record()
+        dbw()
+        e[1].record()
+        cbw()
+        e[2].record()
+    torch.cuda.synchronize()
+    ms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(2)] for e in ev])
+    d_us, c_us = np.median(ms, axis=0) * 1e3
+    db, cb = bytes_dispatch_backward(w), bytes_combine_backward(w)
+    return {"dispatch_backward": {"us": round(float(d_us), 2), "bytes": db, "GBps": round(db / d_us / 1e3, 1)},
+            "combine_backward": {"us": round(float(c_us), 2), "bytes": cb, "GBps": round(cb / c_us / 1e3, 1)},
+            "note": f"medians of {reps} calls with events around each, on the step's routing handle; "
+                    "combine_backward includes the gate-weight gradient"}
 
 
 def pct(a, q):
@@ -343,6 +389,9 @@ def main():
     cold_stage = time_stages(step, 20, flush)
     cold_us = float(np.median(cold_step)) * 1e3
 
+    log("[bench] backward pair")
+    backward = time_backward(step, 20)
+
     dec = None
     if not args.no_decode:
         log("[bench] decode workload")
@@ -414,6 +463,7 @@ def main():
         "copy_ceiling": {"GBps": round(copy_gbps, 1), "kernel": "torch bitwise_not, 1 GiB in + 1 GiB out",
                          "step_frac_of_copy": round(value / copy_gbps, 4)},
         "decode": dec,
+        "backward": backward,
         "configs": configs,
         "cpu_baseline": cb,
         "wall_s_timed": round(wall, 4),

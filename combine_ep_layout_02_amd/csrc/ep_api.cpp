@@ -9,6 +9,8 @@
 
 #define EP_EXPORT extern "C" __attribute__((visibility("default")))
 
+static_assert(ep::kMaxTopk == EP_MAX_TOPK, "device top-k limit must match the ABI's");
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -162,6 +164,52 @@ EP_EXPORT ep_status_t ep_combine(const ep_shape_t* shape, const void* y, const i
   p.k = shape->num_topk;
   p.rows = recv_rows_of(shape);
   return hip_status(ep::launch_combine(p, stream));
+}
+
+EP_EXPORT ep_status_t ep_dispatch_backward(const ep_shape_t* shape, const void* grad_recv_x, const int32_t* slot,
+                                           void* grad_x, hipStream_t stream) {
+  const ep_status_t st = check_shape(shape);
+  if (st != EP_OK) return st;
+  const int T = shape->num_tokens;
+  if (T == 0) return EP_OK;
+  if (!grad_recv_x || !slot || !grad_x) return EP_ERR_INVALID_ARG;
+  if (!aligned(grad_recv_x, 16) || !aligned(grad_x, 16) || !aligned(slot, 4)) return EP_ERR_MISALIGNED;
+  ep::RowParams p{};
+  p.src = grad_recv_x;
+  p.slot = slot;
+  p.weights = nullptr;  // unit weights
+  p.dst = grad_x;
+  p.T = T;
+  p.H = shape->hidden;
+  p.k = shape->num_topk;
+  p.rows = recv_rows_of(shape);
+  return hip_status(ep::launch_combine(p, stream));
+}
+
+EP_EXPORT ep_status_t ep_combine_backward(const ep_shape_t* shape, const void* grad_out, const void* y,
+                                          const int32_t* slot, const float* topk_weights, void* grad_y,
+                                          float* grad_weights, hipStream_t stream) {
+  const ep_status_t st = check_shape(shape);
+  if (st != EP_OK) return st;
+  const int T = shape->num_tokens;
+  if (T == 0) return EP_OK;
+  if (!grad_out || !slot || !topk_weights || !grad_y) return EP_ERR_INVALID_ARG;
+  if (grad_weights && !y) return EP_ERR_INVALID_ARG;
+  if (!aligned(grad_out, 16) || !aligned(y, 16) || !aligned(grad_y, 16) || !aligned(slot, 4) ||
+      !aligned(topk_weights, 4) || !aligned(grad_weights, 4))
+    return EP_ERR_MISALIGNED;
+  ep::BackParams p{};
+  p.g = grad_out;
+  p.y = y;
+  p.slot = slot;
+  p.weights = topk_weights;
+  p.grad_y = grad_y;
+  p.grad_w = grad_weights;
+  p.T = T;
+  p.H = shape->hidden;
+  p.k = shape->num_topk;
+  p.rows = recv_rows_of(shape);
+  return hip_status(ep::launch_combine_backward(p, stream));
 }
 
 EP_EXPORT ep_status_t ep_check_cvt_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {

@@ -9,6 +9,11 @@
 // round to nearest even (v_cvt_pk_bf16_f32).  A fixed order keeps the result
 // deterministic and equal to a scalar evaluation of the same chain.
 //
+// With no weights (every weight 1) the same kernel is the backward of
+// dispatch: the gradient of a token is the sum of the gradients of its
+// received copies (DeepEP runs the backward of dispatch as a combine:
+// documentation item 10, "Backward Pass"), and fmaf(1, v, acc) == acc + v.
+//
 // Work unit: one wavefront per (token, column chunk).  All k row loads
 // (16 bytes per lane and column group each) are issued before the first FMA,
 // so a wavefront keeps k * groups independent 1 KiB reads in flight.  Slots
@@ -91,7 +96,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void combine_kernel(RowParams 
   int sl = -1, wl = 0;
   if (lane < k) {
     sl = p.slot[(int64_t)t * k + lane];
-    wl = (int)__float_as_uint(p.weights[(int64_t)t * k + lane]);
+    wl = (int)__float_as_uint(p.weights ? p.weights[(int64_t)t * k + lane] : 1.0f);
   }
   const uint16_t* y = static_cast<const uint16_t*>(p.src);
   float acc[kGroups][8];

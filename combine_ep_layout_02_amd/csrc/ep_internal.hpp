@@ -44,16 +44,33 @@ hipError_t launch_layout(const LayoutPlan& plan, LayoutParams p, hipStream_t str
 struct RowParams {
   const void* src;          // x (dispatch) or y (combine)
   const int32_t* slot;
-  const float* weights;     // combine only
+  const float* weights;     // combine only; null = every weight 1 (dispatch backward)
   void* dst;                // recv_x (dispatch) or out (combine)
   float* recv_scale;        // FP8 dispatch only
   int T, H, k;
   int64_t rows;             // receive rows (bounds for slot values)
 };
 
+// Combine backward: g [T, H] and y [rows, H] BF16, grad_y [rows, H] BF16,
+// grad_w [T, k] fp32 or null (then y is not read).
+struct BackParams {
+  const void* g;
+  const void* y;
+  const int32_t* slot;
+  const float* weights;
+  void* grad_y;
+  float* grad_w;
+  int T, H, k;
+  int64_t rows;
+};
+
+// Upper bound of num_topk (the C ABI's EP_MAX_TOPK), for LDS sizing.
+constexpr int kMaxTopk = 64;
+
 hipError_t launch_dispatch_bf16(const RowParams& p, hipStream_t stream);
 hipError_t launch_dispatch_fp8(const RowParams& p, hipStream_t stream);
-hipError_t launch_combine(const RowParams& p, hipStream_t stream);
+hipError_t launch_combine(const RowParams& p, hipStream_t stream);  // weights null: unit weights
+hipError_t launch_combine_backward(const BackParams& p, hipStream_t stream);
 
 hipError_t launch_check_cvt_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 hipError_t launch_check_cvt_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream);

@@ -27,8 +27,8 @@ EP_MAX_EXPERTS = 2048
 EP_MAX_TOPK = 64
 
 EXPORTED = ("ep_recv_rows", "ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_combine",
-            "ep_status_string", "ep_abi_version", "ep_last_hip_error", "ep_check_cvt_e4m3",
-            "ep_check_cvt_bf16")
+            "ep_dispatch_backward", "ep_combine_backward", "ep_status_string", "ep_abi_version",
+            "ep_last_hip_error", "ep_check_cvt_e4m3", "ep_check_cvt_bf16")
 
 
 class EpError(RuntimeError):
@@ -104,6 +104,10 @@ def lib() -> ctypes.CDLL:
         L.ep_dispatch.argtypes = [sp, vp, vp, ctypes.c_int, vp, vp, vp]
         L.ep_combine.restype = st
         L.ep_combine.argtypes = [sp, vp, vp, vp, vp, vp]
+        L.ep_dispatch_backward.restype = st
+        L.ep_dispatch_backward.argtypes = [sp, vp, vp, vp, vp]
+        L.ep_combine_backward.restype = st
+        L.ep_combine_backward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp]
         L.ep_check_cvt_e4m3.restype = st
         L.ep_check_cvt_e4m3.argtypes = [vp, vp, ctypes.c_int64, vp]
         L.ep_check_cvt_bf16.restype = st
@@ -218,6 +222,39 @@ def ep_combine(shape: EpShape, y, slot, topk_weights, out, stream=None) -> None:
         _ptr(out, "out", _BF16_LIKE, T * H, optional=T == 0), _stream(stream)))
 
 
+def _dispatch_backward_args(shape: EpShape, grad_recv_x, slot, grad_x):
+    T, H, k = shape.num_tokens, shape.hidden, shape.num_topk
+    rows = shape.recv_rows
+    return (shape.c_ref, _ptr(grad_recv_x, "grad_recv_x", _BF16_LIKE, rows * H, optional=T == 0),
+            _ptr(slot, "slot", torch.int32, T * k, optional=T == 0),
+            _ptr(grad_x, "grad_x", _BF16_LIKE, T * H, optional=T == 0))
+
+
+def _combine_backward_args(shape: EpShape, grad_out, y, slot, topk_weights, grad_y, grad_weights):
+    T, H, k = shape.num_tokens, shape.hidden, shape.num_topk
+    rows = shape.recv_rows
+    return (shape.c_ref, _ptr(grad_out, "grad_out", _BF16_LIKE, T * H, optional=T == 0),
+            _ptr(y, "y", _BF16_LIKE, rows * H, optional=T == 0 or grad_weights is None),
+            _ptr(slot, "slot", torch.int32, T * k, optional=T == 0),
+            _ptr(topk_weights, "topk_weights", torch.float32, T * k, optional=T == 0),
+            _ptr(grad_y, "grad_y", _BF16_LIKE, rows * H, optional=T == 0),
+            _ptr(grad_weights, "grad_weights", torch.float32, T * k, optional=True))
+
+
+def ep_dispatch_backward(shape: EpShape, grad_recv_x, slot, grad_x, stream=None) -> None:
+    """grad_x[t] = BF16(sum over valid j of grad_recv_x[slot[t, j]]) (unit-weight combine)."""
+    _check("ep_dispatch_backward",
+           lib().ep_dispatch_backward(*_dispatch_backward_args(shape, grad_recv_x, slot, grad_x), _stream(stream)))
+
+
+def ep_combine_backward(shape: EpShape, grad_out, y, slot, topk_weights, grad_y, grad_weights=None,
+                        stream=None) -> None:
+    """grad_y[slot[t, j]] = BF16(w[t, j] * grad_out[t]); grad_weights[t, j] = <grad_out[t], y[slot[t, j]]>
+    (skipped, and y unused, when grad_weights is None)."""
+    _check("ep_combine_backward", lib().ep_combine_backward(
+        *_combine_backward_args(shape, grad_out, y, slot, topk_weights, grad_y, grad_weights), _stream(stream)))
+
+
 def ep_check_cvt_e4m3(inp, out, stream=None) -> None:
     n = inp.numel()
     _check("ep_check_cvt_e4m3", lib().ep_check_cvt_e4m3(
@@ -301,6 +338,18 @@ def prepare_combine(shape: EpShape, y, slot, topk_weights, out, stream=None) -> 
             _ptr(topk_weights, "topk_weights", torch.float32, T * k, optional=T == 0),
             _ptr(out, "out", _BF16_LIKE, T * H, optional=T == 0))
     return Prepared("ep_combine", lib().ep_combine, args, (y, slot, topk_weights, out), stream)
+
+
+def prepare_dispatch_backward(shape: EpShape, grad_recv_x, slot, grad_x, stream=None) -> Prepared:
+    return Prepared("ep_dispatch_backward", lib().ep_dispatch_backward,
+                    _dispatch_backward_args(shape, grad_recv_x, slot, grad_x), (grad_recv_x, slot, grad_x), stream)
+
+
+def prepare_combine_backward(shape: EpShape, grad_out, y, slot, topk_weights, grad_y, grad_weights=None,
+                             stream=None) -> Prepared:
+    return Prepared("ep_combine_backward", lib().ep_combine_backward,
+                    _combine_backward_args(shape, grad_out, y, slot, topk_weights, grad_y, grad_weights),
+                    (grad_out, y, slot, topk_weights, grad_y, grad_weights), stream)
 
 
 # ---------------------------------------------------------------------------

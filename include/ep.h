@@ -12,6 +12,14 @@
  *   ep_combine   gather expert outputs back to token order as the gate-
  *                weighted fp32 sum of the top-k rows, written as BF16.
  *
+ * and the backward pair over the same routing handle:
+ *
+ *   ep_dispatch_backward  gradient of the tokens: the unit-weight combine of
+ *                         the received rows' gradients.
+ *   ep_combine_backward   gradients of the expert outputs (a dispatch of the
+ *                         output gradient, scaled per copy) and of the gate
+ *                         weights.
+ *
  * Sources for what the operations are (the pages print no code):
  *   [GN]  GeekNews "DeepSeek publica DeepEP, una biblioteca open source para
  *         entrenamiento e inferencia MoE" (es.news.hada.io), sections
@@ -47,7 +55,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 1
+#define EP_ABI_VERSION 2
 
 /* Limits checked by every entry point (EP_ERR_UNSUPPORTED beyond them). */
 #define EP_MAX_EXPERTS 2048
@@ -179,6 +187,50 @@ ep_status_t ep_dispatch(const ep_shape_t *shape, const void *x, const int32_t *s
  */
 ep_status_t ep_combine(const ep_shape_t *shape, const void *y, const int32_t *slot,
                        const float *topk_weights, void *out, hipStream_t stream);
+
+/*
+ * Backward of dispatch.  DeepEP runs it as a combine over the same handle
+ * ([DOC] item 10, "Backward Pass"; [GN] "Patrones de uso ...").  Forward,
+ * every valid pair's row is a copy of x[t], so the gradient of x[t] is the
+ * sum of its copies' gradients:
+ *   grad_x[t, h] = BF16_RNE( acc ),  acc = +0, then for j = 0..k-1 with
+ *                  slot[t, j] >= 0:  acc = acc + grad_recv_x[slot[t, j], h]
+ * (fp32, ascending j): ep_combine with every weight 1, bit for bit.  Pairs
+ * that are masked or were dropped by a padded layout contribute nothing.
+ * For FP8 dispatch the quantisation is passed through as the identity.
+ *
+ *   grad_recv_x  BF16 [ep_recv_rows, H]  gradient of the received rows
+ *   slot         int32 [T, k]            from ep_layout
+ *   grad_x       BF16 [T, H]
+ */
+ep_status_t ep_dispatch_backward(const ep_shape_t *shape, const void *grad_recv_x,
+                                 const int32_t *slot, void *grad_x, hipStream_t stream);
+
+/*
+ * Backward of combine.  DeepEP runs it as a dispatch over the same handle
+ * ([DOC] item 10, "Backward Pass"; [GN] "Patrones de uso ...").  Forward,
+ * out[t] = sum over valid j of w[t, j] * y[slot[t, j]] (its BF16 rounding is
+ * passed through as the identity), so for g = d loss / d out:
+ *   grad_y[slot[t, j], h] = BF16_RNE( w[t, j] * g[t, h] )  (fp32 product)
+ *   grad_weights[t, j]    = sum over h of g[t, h] * y[slot[t, j], h]  (fp32)
+ * grad_y rows that no valid pair maps to are left untouched;
+ * grad_weights of a masked or dropped pair is 0.  grad_y is exact to the
+ * definition.  grad_weights is summed in a fixed, deterministic tree; it
+ * lies within (H/64 + 16) * 2^-24 * sum_h |g[t, h] * y[slot[t, j], h]| of
+ * the exact dot product (every BF16 x BF16 product is exact in fp32).
+ *
+ *   grad_out      BF16 [T, H]             g
+ *   y             BF16 [ep_recv_rows, H]  the expert outputs combine read;
+ *                                         may be NULL if grad_weights is NULL
+ *   slot          int32 [T, k]            from ep_layout
+ *   topk_weights  fp32 [T, k]             the gate weights combine used
+ *   grad_y        BF16 [ep_recv_rows, H]
+ *   grad_weights  fp32 [T, k], or NULL to skip the weight gradient (then y
+ *                 is not read)
+ */
+ep_status_t ep_combine_backward(const ep_shape_t *shape, const void *grad_out, const void *y,
+                                const int32_t *slot, const float *topk_weights, void *grad_y,
+                                float *grad_weights, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *ep_status_string(ep_status_t status);

@@ -50,12 +50,12 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert ep.ep_abi_version() == 1
+    header = open(HEADER).read()
+    assert ep.ep_abi_version() == int(re.search(r"#define EP_ABI_VERSION (\d+)", header).group(1)) == 2
     for code in range(6):
         s = ep.ep_status_string(code)
         assert s.startswith("EP_"), s
     assert "unknown" in ep.ep_status_string(42)
-    header = open(HEADER).read()
     assert "#define EP_MAX_EXPERTS %d" % epmod.EP_MAX_EXPERTS in header
     assert "#define EP_MAX_TOPK %d" % epmod.EP_MAX_TOPK in header
 
@@ -105,6 +105,8 @@ def test_bad_shapes_rejected(L, kw, code):
     assert L.ep_layout(ctypes.byref(shape_c(**kw)), *([None] * 9), 0, None) == code
     assert L.ep_dispatch(ctypes.byref(shape_c(**kw)), None, None, 0, None, None, None) == code
     assert L.ep_combine(ctypes.byref(shape_c(**kw)), None, None, None, None, None) == code
+    assert L.ep_dispatch_backward(ctypes.byref(shape_c(**kw)), None, None, None, None) == code
+    assert L.ep_combine_backward(ctypes.byref(shape_c(**kw)), *([None] * 6), None) == code
 
 
 def test_null_shape_and_outputs(L):
@@ -164,6 +166,37 @@ def test_combine_argument_checks(L):
     assert L.ep_combine(s, FAKE, FAKE, FAKE, FAKE + 8, None) == MISALIGNED
     assert L.ep_combine(s, FAKE, FAKE + 1, FAKE, FAKE, None) == MISALIGNED
     assert L.ep_combine(ctypes.byref(shape_c(num_tokens=0)), None, None, None, None, None) == OK
+
+
+def test_dispatch_backward_argument_checks(L):
+    s = ctypes.byref(shape_c())
+    for i in range(3):
+        q = [FAKE] * 3
+        q[i] = None
+        assert L.ep_dispatch_backward(s, *q, None) == INVALID
+    assert L.ep_dispatch_backward(s, FAKE + 8, FAKE, FAKE, None) == MISALIGNED     # grad_recv_x 16-byte
+    assert L.ep_dispatch_backward(s, FAKE, FAKE + 2, FAKE, None) == MISALIGNED     # slot 4-byte
+    assert L.ep_dispatch_backward(s, FAKE, FAKE, FAKE + 8, None) == MISALIGNED     # grad_x 16-byte
+    assert L.ep_dispatch_backward(ctypes.byref(shape_c(num_tokens=0)), None, None, None, None) == OK
+
+
+def test_combine_backward_argument_checks(L):
+    s = ctypes.byref(shape_c())
+    # grad_out, y, slot, topk_weights, grad_y, grad_weights
+    for i in (0, 2, 3, 4):
+        q = [FAKE] * 6
+        q[i] = None
+        assert L.ep_combine_backward(s, *q, None) == INVALID
+    q = [FAKE] * 6
+    q[1] = None   # y is needed for grad_weights ...
+    assert L.ep_combine_backward(s, *q, None) == INVALID
+    q[5] = None   # ... and not without them (nothing is launched for T = 0 below)
+    assert L.ep_combine_backward(ctypes.byref(shape_c(num_tokens=0)), *q, None) == OK
+    for i, off in ((0, 8), (1, 8), (2, 2), (3, 2), (4, 8), (5, 2)):
+        q = [FAKE] * 6
+        q[i] += off
+        assert L.ep_combine_backward(s, *q, None) == MISALIGNED, i
+    assert L.ep_combine_backward(ctypes.byref(shape_c(num_tokens=0)), *([None] * 6), None) == OK
 
 
 def test_check_helpers_argument_checks(L):

@@ -1,0 +1,194 @@
+"""GPU parity of the backward pair, through the C ABI, against the CPU oracle.
+
+ep_dispatch_backward must match the oracle bit for bit (a fixed-order fp32
+sum, like combine).  ep_combine_backward's grad_y must match bit for bit (one
+fp32 product and one BF16 rounding per element); its grad_weights must lie
+within the fp32 summation bound stated in include/ep.h of the oracle's exact
+dot product, and be deterministic.  Inputs come from the seeded generators
+only; no expected value comes from the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import combine_ep_layout_02_amd as ep
+from combine_ep_layout_02_amd import workloads as wl
+from test_gpu_parity import (DEV, _idx, bf16_ulp_distance, dev_bf16, dev_f32, dev_i32, host_u16, inputs, log,
+                             setup_module, shape_of)  # noqa: F401  (setup_module builds the library)
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0x7BAD
+
+
+def gw_bound(g_bits, y_bits, slot, H):
+    """(H/64 + 16) * 2^-24 * sum_h |g[t,h] * y[slot[t,j],h]| per pair (0 for masked pairs)."""
+    gf = np.abs(wl.bf16_bits_to_f32(g_bits).astype(np.float64))
+    yf = np.abs(wl.bf16_bits_to_f32(y_bits[np.maximum(slot, 0)]).astype(np.float64))   # [T, k, H]
+    mag = (yf * gf[:, None, :]).sum(-1)
+    return (H / 64 + 16) * 2.0 ** -24 * np.where(slot >= 0, mag, 0.0)
+
+
+def run_dispatch_backward(w, grad_bits, slot):
+    out = torch.full((w.num_tokens, w.hidden), SENTINEL, dtype=torch.int16, device=DEV)
+    ep.ep_dispatch_backward(shape_of(w), dev_bf16(grad_bits), dev_i32(slot), out)
+    torch.cuda.synchronize()
+    return host_u16(out)
+
+
+def run_combine_backward(w, g_bits, y_bits, slot, weights, want_gw=True):
+    shape = shape_of(w)
+    gy = torch.full((w.recv_rows, w.hidden), SENTINEL, dtype=torch.int16, device=DEV)
+    gw = torch.full((w.num_tokens, w.num_topk), float("nan"), dtype=torch.float32, device=DEV) if want_gw else None
+    ep.ep_combine_backward(shape, dev_bf16(g_bits), dev_bf16(y_bits) if want_gw else None, dev_i32(slot),
+                           dev_f32(weights), gy, gw)
+    torch.cuda.synchronize()
+    return host_u16(gy), (gw.cpu().numpy() if want_gw else None)
+
+
+def check_combine_backward(w, g, y, slot, wts, gy, gw, tokens=None):
+    """Compare against the oracle, on all tokens or on the sampled ones."""
+    if tokens is None:
+        tokens = np.arange(w.num_tokens)
+    s = slot[tokens]
+    want_gy, want_gw = oracle.combine_backward(g[tokens], y, s, wts[tokens],
+                                               np.full(y.shape, SENTINEL, np.uint16))
+    held = np.zeros(w.recv_rows, bool)
+    held[s[s >= 0]] = True
+    assert np.array_equal(gy[held], want_gy[held])
+    if len(tokens) == w.num_tokens:
+        assert (gy[~held] == SENTINEL).all()   # rows no pair maps to are untouched
+    if gw is not None:
+        err = np.abs(gw[tokens].astype(np.float64) - want_gw)
+        bound = gw_bound(g[tokens], y, s, w.hidden)
+        log(f"  grad_w max err {err.max():.3g}, max err/bound {np.max(err / np.maximum(bound, 1e-300)):.3g}")
+        assert (err <= bound).all()
+        assert (gw[tokens][s < 0] == 0).all()
+
+
+# --------------------------------------------------------------------------
+# dispatch backward
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(wl.WORKLOADS))
+def test_dispatch_backward_matches_oracle(name):
+    w, inp, lay = inputs(name, with_y=True)   # y serves as the received rows' gradient
+    log(f"[dispatch-bwd] {name}")
+    got = run_dispatch_backward(w, inp.y, lay.slot)
+    want = oracle.dispatch_backward(inp.y, lay.slot)
+    assert (bf16_ulp_distance(got, want) == 0).all()
+
+
+DISPATCH_BWD_EDGE = [
+    # name, T, H, k, E, R, A, C, mask
+    ("k3_generic_masked", 300, 640, 3, 16, 4, 1, 0, 0.1),
+    ("k64_generic", 32, 256, 64, 64, 8, 1, 0, 0.0),
+    ("padded_drops", 300, 1024, 4, 16, 4, 1, 40, 0.0),
+    ("h136_aligned", 100, 136, 2, 8, 2, 4, 0, 0.0),
+    ("one_token", 1, 7168, 8, 256, 8, 1, 0, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", DISPATCH_BWD_EDGE, ids=lambda c: c[0])
+def test_dispatch_backward_edge_cases(case):
+    name, T, H, k, E, R, A, C, mask = case
+    log(f"[dispatch-bwd-edge] {name}")
+    w = wl.custom(name, T, H, E, R, k, seed=93, capacity=C, expert_alignment=A)
+    rng = np.random.default_rng(93)
+    lay = oracle.layout(_idx(rng, T, k, E, mask), E, R, A, C)
+    G = wl.normal_bf16(93, 2, w.recv_rows, H)
+    got = run_dispatch_backward(w, G, lay.slot)
+    assert (bf16_ulp_distance(got, oracle.dispatch_backward(G, lay.slot)) == 0).all()
+
+
+def test_dispatch_backward_is_adjoint_of_dispatch_at_full_size():
+    """<dispatch(x), G> == <x, dispatch_backward(G)> with small-integer data (every
+    sum exact), on the 8192-token workload: a property that holds at any size."""
+    w, inp, lay = inputs("v3")
+    shape = shape_of(w)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(5)
+    x = torch.randint(-3, 4, (w.num_tokens, w.hidden), generator=gen, device=DEV).to(torch.bfloat16)
+    G = torch.randint(-3, 4, (w.recv_rows, w.hidden), generator=gen, device=DEV).to(torch.bfloat16)
+    bufs = ep.LayoutBuffers.allocate(shape, DEV).run(dev_i32(inp.topk_idx))
+    rx, _ = ep.alloc_recv(shape, ep.EP_BF16, DEV)
+    ep.ep_dispatch(shape, x, bufs.slot, ep.EP_BF16, rx)
+    gx = torch.empty_like(x)
+    ep.ep_dispatch_backward(shape, G, bufs.slot, gx)
+    torch.cuda.synchronize()
+    lhs = (rx.double() * G.double()).sum().item()
+    rhs = (x.double() * gx.double()).sum().item()
+    assert lhs == rhs
+
+
+# --------------------------------------------------------------------------
+# combine backward
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "decode", "v3", "skew"])
+def test_combine_backward_matches_oracle(name):
+    w, inp, lay = inputs(name, with_y=True)
+    g = wl.normal_bf16(w.seed, 5, w.num_tokens, w.hidden)   # output gradient: its own stream
+    log(f"[combine-bwd] {name}")
+    gy, gw = run_combine_backward(w, g, inp.y, lay.slot, inp.topk_weights)
+    # full comparison where the oracle takes seconds; 384 sampled tokens at 8K and 16K tokens
+    tokens = None
+    if w.num_tokens > 4096:
+        tokens = np.sort(np.random.default_rng(w.seed).choice(w.num_tokens, 384, replace=False))
+    check_combine_backward(w, g, inp.y, lay.slot, inp.topk_weights, gy, gw, tokens)
+    # deterministic: the same call gives the same bits
+    gy2, gw2 = run_combine_backward(w, g, inp.y, lay.slot, inp.topk_weights)
+    assert np.array_equal(gy, gy2) and np.array_equal(gw.view(np.uint32), gw2.view(np.uint32))
+
+
+COMBINE_BWD_EDGE = [
+    # name, T, H, k, E, R, A, C, mask, want_gw
+    ("k3_generic_masked", 300, 640, 3, 16, 4, 1, 0, 0.1, True),
+    ("k16_generic", 64, 1024, 16, 64, 8, 1, 0, 0.05, True),
+    ("k64_generic", 16, 256, 64, 64, 8, 1, 0, 0.0, True),
+    ("padded_drops", 300, 1024, 4, 16, 4, 1, 40, 0.0, True),
+    ("h136_aligned", 100, 136, 2, 8, 2, 4, 0, 0.0, True),
+    ("h16384_loops", 24, 16384, 8, 64, 8, 1, 0, 0.0, True),
+    ("h9216", 40, 9216, 6, 64, 8, 1, 0, 0.0, True),
+    ("no_grad_weights", 200, 2048, 8, 64, 8, 1, 0, 0.1, False),
+    ("no_grad_weights_generic_k5", 100, 512, 5, 16, 4, 1, 0, 0.0, False),
+    ("one_token", 1, 7168, 8, 256, 8, 1, 0, 0.0, True),
+]
+
+
+@pytest.mark.parametrize("case", COMBINE_BWD_EDGE, ids=lambda c: c[0])
+def test_combine_backward_edge_cases(case):
+    name, T, H, k, E, R, A, C, mask, want_gw = case
+    log(f"[combine-bwd-edge] {name}")
+    w = wl.custom(name, T, H, E, R, k, seed=94, capacity=C, expert_alignment=A)
+    rng = np.random.default_rng(94)
+    lay = oracle.layout(_idx(rng, T, k, E, mask), E, R, A, C)
+    y = wl.normal_bf16(94, 2, w.recv_rows, H)
+    g = wl.normal_bf16(94, 5, T, H)
+    wts = rng.standard_normal((T, k)).astype(np.float32)
+    gy, gw = run_combine_backward(w, g, y, lay.slot, wts, want_gw)
+    check_combine_backward(w, g, y, lay.slot, wts, gy, gw)
+
+
+def test_combine_backward_is_adjoint_of_combine_at_full_size():
+    """<combine(y, w), g> == <y, grad_y> with small-integer y, g and weights in {0.5, 1}
+    (every value exact), on the 8192-token workload."""
+    w, inp, lay = inputs("v3")
+    shape = shape_of(w)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(6)
+    y = torch.randint(-3, 4, (w.recv_rows, w.hidden), generator=gen, device=DEV).to(torch.bfloat16)
+    g = torch.randint(-3, 4, (w.num_tokens, w.hidden), generator=gen, device=DEV).to(torch.bfloat16)
+    wts = (torch.randint(1, 3, (w.num_tokens, w.num_topk), generator=gen, device=DEV).float() * 0.5)
+    bufs = ep.LayoutBuffers.allocate(shape, DEV).run(dev_i32(inp.topk_idx))
+    out = torch.empty_like(g)
+    ep.ep_combine(shape, y, bufs.slot, wts, out)
+    gy = torch.zeros_like(y)
+    gw = torch.empty_like(wts)
+    ep.ep_combine_backward(shape, g, y, bufs.slot, wts, gy, gw)
+    torch.cuda.synchronize()
+    assert (out.double() * g.double()).sum().item() == (y.double() * gy.double()).sum().item()
+    # integer data: every dot product is exact in fp32 too
+    want = (y[bufs.slot.long()].double() * g.double()[:, None, :]).sum(-1)
+    assert torch.equal(gw.double(), want)

@@ -69,8 +69,21 @@ __device__ __forceinline__ void load_row(const RowParams& p, const Slice& sl, in
     v[c] = load16<AUX_LD>(rx, c < sl.nc ? (uint32_t)((sl.c0 + c) * 512 + lane * 8) * 2u : kNoColumn);
 }
 
+// Eight BF16 values times w, each product rounded to fp32 and then to BF16
+// (nearest even).
+__device__ __forceinline__ u32x4 scale8(u32x4 v, float w) {
+  u32x4 o;
+  o.x = pack_bf16x2(w * bf16_lo(v.x), w * bf16_hi(v.x));
+  o.y = pack_bf16x2(w * bf16_lo(v.y), w * bf16_hi(v.y));
+  o.z = pack_bf16x2(w * bf16_lo(v.z), w * bf16_hi(v.z));
+  o.w = pack_bf16x2(w * bf16_lo(v.w), w * bf16_hi(v.w));
+  return o;
+}
+
 // NC: chunk capacity of the instantiation (>= chunks per wavefront).
-template <int NC, int AUX_LD, int AUX_ST>
+// SCALED: copy j is BF16_RNE(w[t,j] * x[t]) instead of x[t] (the output-row
+// gradients of the combine backward: a dispatch scaled per copy).
+template <int NC, int AUX_LD, int AUX_ST, bool SCALED>
 __global__ __launch_bounds__(256) void dispatch_bf16_kernel(RowParams p, int wpt, int cpw, int nchunks) {
   const int lane = threadIdx.x & 63;
   Slice sl;
@@ -78,6 +91,8 @@ __global__ __launch_bounds__(256) void dispatch_bf16_kernel(RowParams p, int wpt
   u32x4 v[NC];
   load_row<NC, AUX_LD>(p, sl, lane, v);
   const int slots = load_lane_slot(p.slot, sl.t, p.k, lane);
+  int wl = 0;
+  if (SCALED && lane < p.k) wl = (int)__float_as_uint(p.weights[(int64_t)sl.t * p.k + lane]);
 
   uint16_t* dst = static_cast<uint16_t*>(p.dst);
   const uint32_t col = (uint32_t)(sl.c0 * 512 + lane * 8) * 2u;
@@ -85,9 +100,16 @@ __global__ __launch_bounds__(256) void dispatch_bf16_kernel(RowParams p, int wpt
     const int s = __builtin_amdgcn_readlane(slots, j);
     if (!slot_ok(s, p.rows)) continue;
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(dst + (int64_t)s * p.H, (uint32_t)p.H * 2u);
+    if constexpr (SCALED) {
+      const float w = __uint_as_float((uint32_t)__builtin_amdgcn_readlane(wl, j));
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      if (c < sl.nc) store16<AUX_ST>(rd, col + 1024u * c, v[c]);
+      for (int c = 0; c < NC; ++c)
+        if (c < sl.nc) store16<AUX_ST>(rd, col + 1024u * c, scale8(v[c], w));
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        if (c < sl.nc) store16<AUX_ST>(rd, col + 1024u * c, v[c]);
+    }
   }
 }
 
@@ -218,14 +240,22 @@ Split split_for(const RowParams& p) {
 
 namespace {
 
+template <int NC, bool SCALED>
+void launch_bf16_ncs(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  if (streaming)
+    hipLaunchKernelGGL((dispatch_bf16_kernel<NC, kAuxDefault, kAuxNT, SCALED>), dim3(s.blocks), dim3(256), 0, stream,
+                       p, s.wpt, s.cpw, s.nchunks);
+  else
+    hipLaunchKernelGGL((dispatch_bf16_kernel<NC, kAuxDefault, kAuxDefault, SCALED>), dim3(s.blocks), dim3(256), 0,
+                       stream, p, s.wpt, s.cpw, s.nchunks);
+}
+
 template <int NC>
 void launch_bf16_nc(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
-  if (streaming)
-    hipLaunchKernelGGL((dispatch_bf16_kernel<NC, kAuxDefault, kAuxNT>), dim3(s.blocks), dim3(256), 0, stream, p,
-                       s.wpt, s.cpw, s.nchunks);
+  if (p.weights)
+    launch_bf16_ncs<NC, true>(s, p, streaming, stream);
   else
-    hipLaunchKernelGGL((dispatch_bf16_kernel<NC, kAuxDefault, kAuxDefault>), dim3(s.blocks), dim3(256), 0, stream,
-                       p, s.wpt, s.cpw, s.nchunks);
+    launch_bf16_ncs<NC, false>(s, p, streaming, stream);
 }
 
 template <int NC>

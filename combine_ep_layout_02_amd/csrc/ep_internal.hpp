@@ -44,7 +44,8 @@ hipError_t launch_layout(const LayoutPlan& plan, LayoutParams p, hipStream_t str
 struct RowParams {
   const void* src;          // x (dispatch) or y (combine)
   const int32_t* slot;
-  const float* weights;     // combine only; null = every weight 1 (dispatch backward)
+  const float* weights;     // combine: null = every weight 1 (dispatch backward);
+                            // BF16 dispatch: non-null = copy j scaled by w[t,j] (combine backward)
   void* dst;                // recv_x (dispatch) or out (combine)
   float* recv_scale;        // FP8 dispatch only
   int T, H, k;
@@ -67,7 +68,7 @@ struct BackParams {
 // Upper bound of num_topk (the C ABI's EP_MAX_TOPK), for LDS sizing.
 constexpr int kMaxTopk = 64;
 
-hipError_t launch_dispatch_bf16(const RowParams& p, hipStream_t stream);
+hipError_t launch_dispatch_bf16(const RowParams& p, hipStream_t stream);  // weights non-null: scaled copies
 hipError_t launch_dispatch_fp8(const RowParams& p, hipStream_t stream);
 hipError_t launch_combine(const RowParams& p, hipStream_t stream);  // weights null: unit weights
 hipError_t launch_combine_backward(const BackParams& p, hipStream_t stream);

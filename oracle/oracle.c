@@ -41,9 +41,11 @@
  *       s = max(amax, 1e-4) / 448, code = E4M3(x / s), all in fp32;
  *   R9  combine: acc = +0; for j ascending over valid slots
  *       acc = fmaf(w[t,j], y[slot[t,j], h], acc); out = BF16_RNE(acc);
- *   R10 dispatch backward: acc = +0; for j ascending over valid slots
+ *   R10 the scales are row-major fp32 [rows, H/128], on the same row index
+ *       as the receive row they scale;
+ *   R11 dispatch backward: acc = +0; for j ascending over valid slots
  *       acc = acc + grad_recv[slot[t,j], h] (fp32); grad_x = BF16_RNE(acc);
- *   R11 combine backward: grad_y[slot[t,j], h] = BF16_RNE(w[t,j] * g[t,h])
+ *   R12 combine backward: grad_y[slot[t,j], h] = BF16_RNE(w[t,j] * g[t,h])
  *       with the product rounded to fp32 first; grad_w[t,j] = the exact dot
  *       product of g[t] and y[slot[t,j]] (returned in double); the BF16
  *       rounding of the forward output passes the gradient through as is.
@@ -361,7 +363,7 @@ void oracle_combine(int64_t T, int64_t H, int64_t k,
  */
 
 /*
- * Dispatch backward (R10).  Forward, recv[slot[t,j]] = x[t] for each valid
+ * Dispatch backward (R11).  Forward, recv[slot[t,j]] = x[t] for each valid
  * pair, so the gradient of x[t] is the sum of the gradients of its received
  * copies.  Copies that were masked or dropped (slot -1) carry none.  The sum
  * runs in fp32 from +0 in ascending j, rounded once to BF16; it is the
@@ -388,7 +390,7 @@ void oracle_dispatch_backward(int64_t T, int64_t H, int64_t k,
 }
 
 /*
- * Combine backward (R11).  Forward, out[t] = sum over valid j of
+ * Combine backward (R12).  Forward, out[t] = sum over valid j of
  * w[t,j] * y[slot[t,j]], so for the gradient g = d loss / d out:
  *   d/dy[slot[t,j]] = w[t,j] * g[t]      (a dispatch of g, scaled per copy)
  *   d/dw[t,j]       = <g[t], y[slot[t,j]]>

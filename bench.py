@@ -37,6 +37,7 @@ that source is unchanged.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -230,6 +231,95 @@ def time_backward(step, reps):
                     "combine_backward includes the gate-weight gradient"}
 
 
+def cu_sweep(dev, budgets, gemm_n=4096, reps=10):
+    """Dispatch (FP8) and combine on the 8192-token workload under CU budgets
+    (ep_shape_t.num_cus): alone, and beside a BF16 GEMM stream standing in for
+    the expert computation the pages overlap communication with.  0 = the
+    whole GPU."""
+    w = wl.WORKLOADS["v3"]
+    step = Step(w, dev, fp8=True)
+    step.run()
+    s_ep = torch.cuda.current_stream(dev)
+    s_mm = torch.cuda.Stream(dev)        # default priority, like every stream here
+    a = torch.randn((w.num_tokens, w.hidden), device=dev).to(torch.bfloat16)
+    b = torch.randn((w.hidden, gemm_n), device=dev).to(torch.bfloat16)
+    c = torch.empty((w.num_tokens, gemm_n), device=dev, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    gemm_flop = 2.0 * w.num_tokens * w.hidden * gemm_n
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def gemms(n):
+        for _ in range(n):
+            torch.matmul(a, b, out=c)
+
+    # GEMM alone: enough GEMMs to cover the EP work of one measurement
+    with torch.cuda.stream(s_mm):
+        gemms(3)
+        e0, e1 = ev(), ev()
+        e0.record()
+        gemms(20)
+        e1.record()
+    torch.cuda.synchronize()
+    gemm_ms = e0.elapsed_time(e1) / 20
+    rows = []
+    for n in budgets:
+        shape = dataclasses.replace(step.shape, num_cus=n)
+        disp = ep.prepare_dispatch(shape, step.x, step.lay.slot, step.dtype, step.recv_x, step.recv_scale, s_ep)
+        comb = ep.prepare_combine(shape, step.y, step.lay.slot, step.wts, step.out, s_ep)
+        disp()
+        comb()
+        torch.cuda.synchronize()
+        # alone
+        t = []
+        for fn in (disp, comb):
+            e = [(ev(), ev()) for _ in range(reps)]
+            for x0, x1 in e:
+                x0.record(s_ep)
+                fn()
+                x1.record(s_ep)
+            torch.cuda.synchronize()
+            t.append(float(np.median([x0.elapsed_time(x1) for x0, x1 in e])))
+        alone_ms = t[0] + t[1]
+        # beside the GEMM stream: EP pairs on s_ep while GEMMs run on s_mm
+        n_gemm = max(2, int(round(reps * alone_ms / gemm_ms)))
+        g0, g1, p0, p1 = ev(), ev(), ev(), ev()
+        torch.cuda.synchronize()
+        g0.record(s_mm)
+        with torch.cuda.stream(s_mm):
+            gemms(n_gemm)
+        g1.record(s_mm)
+        p0.record(s_ep)
+        for _ in range(reps):
+            disp()
+            comb()
+        p1.record(s_ep)
+        torch.cuda.synchronize()
+        ep_ms = p0.elapsed_time(p1) / reps
+        mm_ms = g0.elapsed_time(g1)
+        both_ms = max(g0.elapsed_time(g1), g0.elapsed_time(p1))
+        serial_ms = n_gemm * gemm_ms + reps * alone_ms
+        rows.append({
+            "num_cus": n,
+            "dispatch_us": round(t[0] * 1e3, 1), "combine_us": round(t[1] * 1e3, 1),
+            "dispatch_GBps": round(bytes_dispatch(w, True) / t[0] / 1e6, 1),
+            "combine_GBps": round(bytes_combine(w) / t[1] / 1e6, 1),
+            "with_gemm": {"ep_pair_us": round(ep_ms * 1e3, 1),
+                          "ep_GBps": round((bytes_dispatch(w, True) + bytes_combine(w)) / ep_ms / 1e6, 1),
+                          "gemm_TFLOPs": round(n_gemm * gemm_flop / mm_ms / 1e9, 1),
+                          "gemms": n_gemm, "overlap_speedup": round(serial_ms / both_ms, 3)},
+        })
+        log(f"[cu-sweep] {rows[-1]}")
+    return {"workload": "v3 (8192 tokens, hidden 7168, top-8; FP8 dispatch, BF16 combine)",
+            "gemm": f"torch.matmul bf16 [{w.num_tokens}, {w.hidden}] x [{w.hidden}, {gemm_n}] on a second stream",
+            "gemm_alone_TFLOPs": round(gemm_flop / gemm_ms / 1e9, 1), "gemm_alone_us": round(gemm_ms * 1e3, 1),
+            "rows": rows,
+            "note": "num_cus = persistent workgroups of up to 1024 threads (0 = one wavefront per work item); "
+                    "ep_pair_us is dispatch + combine per pair while the GEMM stream runs; overlap_speedup = "
+                    "(GEMMs alone + pairs alone) / (both streams together)"}
+
+
 def pct(a, q):
     return round(float(np.percentile(a, q)) * 1e3, 2)
 
@@ -358,6 +448,9 @@ def main():
                     help="skip the tiny, mid and 16K-token skewed workloads")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="counter runs: keep the 1 GiB calibration copy to 3 launches")
+    ap.add_argument("--cu-sweep", nargs="*", type=int, metavar="N",
+                    help="instead of the benchmark: dispatch and combine under CU budgets N (0 = whole GPU), "
+                         "alone and beside a GEMM stream; prints one JSON line")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 counter runs into profiles/combine_v3_traffic.json and exit")
     args = ap.parse_args()
@@ -373,6 +466,10 @@ def main():
         from combine_ep_layout_02_amd.build import build_library
         build_library()
     dev = torch.device("cuda:0")
+    if args.cu_sweep is not None:
+        budgets = args.cu_sweep or [8, 16, 32, 48, 64, 96, 128, 192, 256, 0]
+        print(json.dumps(cu_sweep(dev, budgets)), flush=True)
+        return
 
     w = wl.WORKLOADS[args.workload]
     log(f"[bench] generating {w.name} inputs")

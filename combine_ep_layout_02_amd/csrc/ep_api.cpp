@@ -27,10 +27,14 @@ ep_status_t check_shape(const ep_shape_t* s) {
   if (s->num_experts % s->num_ranks != 0 || s->num_topk > s->num_experts) return EP_ERR_INVALID_ARG;
   if (s->expert_alignment < 1 || s->capacity < 0) return EP_ERR_INVALID_ARG;
   if (s->expert_alignment > 1 && s->capacity > 0) return EP_ERR_INVALID_ARG;
+  if (s->num_cus < 0) return EP_ERR_INVALID_ARG;
+  if (s->num_cus > EP_MAX_NUM_CUS) return EP_ERR_UNSUPPORTED;
   if (s->num_experts > EP_MAX_EXPERTS || s->num_topk > EP_MAX_TOPK) return EP_ERR_UNSUPPORTED;
   if (s->hidden % 8 != 0 || s->hidden > kMaxHidden) return EP_ERR_UNSUPPORTED;
   const int64_t T = s->num_tokens, k = s->num_topk, E = s->num_experts;
   if (T * k >= kMaxRows) return EP_ERR_UNSUPPORTED;
+  // work items (token, 512-column chunk) are counted in int32 on the device
+  if (T * ((s->hidden + 511) / 512) >= kMaxRows) return EP_ERR_UNSUPPORTED;
   const int64_t rows = s->capacity > 0 ? E * s->capacity : T * k + E * (s->expert_alignment - 1);
   if (rows >= kMaxRows) return EP_ERR_UNSUPPORTED;
   return EP_OK;
@@ -141,6 +145,7 @@ EP_EXPORT ep_status_t ep_dispatch(const ep_shape_t* shape, const void* x, const 
   p.H = shape->hidden;
   p.k = shape->num_topk;
   p.rows = recv_rows_of(shape);
+  p.num_cus = shape->num_cus;
   return hip_status(recv_dtype == EP_BF16 ? ep::launch_dispatch_bf16(p, stream)
                                           : ep::launch_dispatch_fp8(p, stream));
 }
@@ -163,6 +168,7 @@ EP_EXPORT ep_status_t ep_combine(const ep_shape_t* shape, const void* y, const i
   p.H = shape->hidden;
   p.k = shape->num_topk;
   p.rows = recv_rows_of(shape);
+  p.num_cus = shape->num_cus;
   return hip_status(ep::launch_combine(p, stream));
 }
 
@@ -183,6 +189,7 @@ EP_EXPORT ep_status_t ep_dispatch_backward(const ep_shape_t* shape, const void* 
   p.H = shape->hidden;
   p.k = shape->num_topk;
   p.rows = recv_rows_of(shape);
+  p.num_cus = shape->num_cus;
   return hip_status(ep::launch_combine(p, stream));
 }
 
@@ -209,6 +216,7 @@ EP_EXPORT ep_status_t ep_combine_backward(const ep_shape_t* shape, const void* g
   p.H = shape->hidden;
   p.k = shape->num_topk;
   p.rows = recv_rows_of(shape);
+  p.num_cus = shape->num_cus;
   return hip_status(ep::launch_combine_backward(p, stream));
 }
 

@@ -74,11 +74,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void grad_weights_kernel(BackParams
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int waves = uniform(blockDim.x >> 6);
-  const int t = blockIdx.x;
   const int H = p.H;
   const int k = K > 0 ? K : p.k;
   const uint32_t row_bytes = (uint32_t)H * 2u;
 
+  // one token per workgroup; a launch limited to a CU budget loops over tokens
+  for (int t = blockIdx.x; t < p.T; t += gridDim.x) {
   const int sl = lane < k ? p.slot[(int64_t)t * k + lane] : -1;
   const uint16_t* y = static_cast<const uint16_t*>(p.y);
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(static_cast<const uint16_t*>(p.g) + (int64_t)t * H, row_bytes);
@@ -127,11 +128,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void grad_weights_kernel(BackParams
     for (int w = 1; w < waves; ++w) acc += part[w][j];
     p.grad_w[(int64_t)t * k + j] = acc;
   }
+  __syncthreads();  // part is rewritten by the next token
+  }
 }
 
 template <int K>
 hipError_t launch_gw(const BackParams& p, int waves, int chunks, hipStream_t stream) {
-  const dim3 grid(p.T), block(64 * waves);
+  const dim3 grid(p.num_cus > 0 && p.num_cus < p.T ? p.num_cus : p.T), block(64 * waves);
   if ((int64_t)p.T * p.k * p.H * 2 < kStreamingBytes)
     hipLaunchKernelGGL((grad_weights_kernel<K, kAuxDefault>), grid, block, 0, stream, p, chunks);
   else
@@ -166,6 +169,7 @@ hipError_t launch_combine_backward(const BackParams& p, hipStream_t stream) {
   r.H = p.H;
   r.k = p.k;
   r.rows = p.rows;
+  r.num_cus = p.num_cus;
   return launch_dispatch_bf16(r, stream);
 }
 

@@ -34,7 +34,7 @@ namespace {
 
 constexpr int kGroups = EP_COMBINE_GROUPS;
 constexpr int kChunk = 512 * kGroups;
-constexpr int kWavesPerBlock = 1;  // 64-thread blocks: measured ~3% faster than 256 at the 8K step
+constexpr int kWavesPerBlock = 1;  // whole-GPU launches: 64-thread blocks, measured ~3% faster than 256 at the 8K step
 
 __device__ __forceinline__ void fma8(float* acc, float w, u32x4 v) {
   acc[0] = __builtin_fmaf(w, bf16_lo(v.x), acc[0]);
@@ -82,12 +82,16 @@ __device__ __forceinline__ void accumulate(const uint16_t* y, int64_t rows, int 
   }
 }
 
-template <int K, int AUX_LD, int AUX_ST>
-__global__ __launch_bounds__(64 * kWavesPerBlock) void combine_kernel(RowParams p, int chunks) {
+// Items (token, chunk) are handed out grid-stride: a whole-GPU launch has one
+// wavefront per item and runs the loop once; a launch limited to a CU budget
+// runs that many persistent workgroups of WPB wavefronts.
+template <int K, int AUX_LD, int AUX_ST, int WPB>
+__global__ __launch_bounds__(64 * WPB) void combine_kernel(RowParams p, int chunks) {
   const int lane = threadIdx.x & 63;
-  const int item = uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const int items = p.T * chunks;
+  for (int item = uniform((int)blockIdx.x * WPB + (int)(threadIdx.x >> 6)); item < items;
+       item += (int)gridDim.x * WPB) {
   const int t = item / chunks;
-  if (t >= p.T) return;
   const int c = item - t * chunks;
   const int H = p.H;
   const int k = K > 0 ? K : p.k;
@@ -115,17 +119,29 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void combine_kernel(RowParams 
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, (uint32_t)H * 2u);
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) store16<AUX_ST>(ro, (col0 + 512u * g) * 2u, pack8(acc[g]));
+  }
+}
+
+template <int K, int WPB>
+void launch_kw(const RowParams& p, int blocks, int chunks, hipStream_t stream) {
+  const dim3 block(64 * WPB);
+  if ((int64_t)p.T * p.k * p.H * 2 < kStreamingBytes)
+    hipLaunchKernelGGL((combine_kernel<K, kAuxDefault, kAuxDefault, WPB>), dim3(blocks), block, 0, stream, p, chunks);
+  else if ((int64_t)p.T * p.H * 2 <= kCacheableOutputBytes)
+    hipLaunchKernelGGL((combine_kernel<K, kAuxNT, kAuxSC1, WPB>), dim3(blocks), block, 0, stream, p, chunks);
+  else
+    hipLaunchKernelGGL((combine_kernel<K, kAuxNT, kAuxNT, WPB>), dim3(blocks), block, 0, stream, p, chunks);
 }
 
 template <int K>
-hipError_t launch_k(const RowParams& p, int blocks, int chunks, hipStream_t stream) {
-  const dim3 block(64 * kWavesPerBlock);
-  if ((int64_t)p.T * p.k * p.H * 2 < kStreamingBytes)
-    hipLaunchKernelGGL((combine_kernel<K, kAuxDefault, kAuxDefault>), dim3(blocks), block, 0, stream, p, chunks);
-  else if ((int64_t)p.T * p.H * 2 <= kCacheableOutputBytes)
-    hipLaunchKernelGGL((combine_kernel<K, kAuxNT, kAuxSC1>), dim3(blocks), block, 0, stream, p, chunks);
-  else
-    hipLaunchKernelGGL((combine_kernel<K, kAuxNT, kAuxNT>), dim3(blocks), block, 0, stream, p, chunks);
+hipError_t launch_k(const RowParams& p, int chunks, hipStream_t stream) {
+  const int64_t items = (int64_t)p.T * chunks;
+  if (p.num_cus > 0) {
+    const int64_t need = (items + kBudgetWaves - 1) / kBudgetWaves;
+    launch_kw<K, kBudgetWaves>(p, (int)(need < p.num_cus ? need : p.num_cus), chunks, stream);
+  } else {
+    launch_kw<K, kWavesPerBlock>(p, (int)((items + kWavesPerBlock - 1) / kWavesPerBlock), chunks, stream);
+  }
   return hipGetLastError();
 }
 
@@ -134,15 +150,13 @@ hipError_t launch_k(const RowParams& p, int blocks, int chunks, hipStream_t stre
 hipError_t launch_combine(const RowParams& p, hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
   const int chunks = (p.H + kChunk - 1) / kChunk;
-  const int64_t items = (int64_t)p.T * chunks;
-  const int blocks = (int)((items + kWavesPerBlock - 1) / kWavesPerBlock);
   switch (p.k) {
-    case 1: return launch_k<1>(p, blocks, chunks, stream);
-    case 2: return launch_k<2>(p, blocks, chunks, stream);
-    case 4: return launch_k<4>(p, blocks, chunks, stream);
-    case 6: return launch_k<6>(p, blocks, chunks, stream);
-    case 8: return launch_k<8>(p, blocks, chunks, stream);
-    default: return launch_k<0>(p, blocks, chunks, stream);
+    case 1: return launch_k<1>(p, chunks, stream);
+    case 2: return launch_k<2>(p, chunks, stream);
+    case 4: return launch_k<4>(p, chunks, stream);
+    case 6: return launch_k<6>(p, chunks, stream);
+    case 8: return launch_k<8>(p, chunks, stream);
+    default: return launch_k<0>(p, chunks, stream);
   }
 }
 

@@ -33,7 +33,7 @@ namespace ep {
 namespace {
 
 constexpr int kMaxChunks = 16;     // most 512-column chunks a wavefront holds (8192 columns)
-constexpr int kWavesPerBlock = 4;  // 256 threads
+constexpr int kWavesPerBlock = 4;  // 256 threads (whole-GPU launches)
 constexpr int kMinWaves = 2048;    // 8 wavefronts per CU
 constexpr uint32_t kNoColumn = 0xFFFFFFF0u;  // a load offset past any row: reads 0
 
@@ -45,20 +45,26 @@ __device__ __forceinline__ int load_lane_slot(const int32_t* slot, int64_t t, in
 
 __device__ __forceinline__ bool slot_ok(int s, int64_t rows) { return s >= 0 && (int64_t)s < rows; }
 
-// Token and first chunk of this wavefront's slice; false past the last token.
+// Token and first chunk of slice `wave` (token-major: wpt slices per token).
 struct Slice {
   int t, c0, nc;
 };
 
-__device__ __forceinline__ bool slice_of(const RowParams& p, int wpt, int cpw, int nchunks, Slice& sl) {
-  const int wave = uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+__device__ __forceinline__ Slice slice_of(int wave, int wpt, int cpw, int nchunks) {
+  Slice sl;
   sl.t = wave / wpt;
-  if (sl.t >= p.T) return false;
-  const int part = wave - sl.t * wpt;
-  sl.c0 = part * cpw;
+  sl.c0 = (wave - sl.t * wpt) * cpw;
   sl.nc = min(cpw, nchunks - sl.c0);
-  return true;
+  return sl;
 }
+
+// Slices are handed out grid-stride: a whole-GPU launch has one wavefront per
+// slice and runs the loop once; a launch limited to a CU budget runs that
+// many persistent workgroups, each wavefront taking every (grid * WPB)-th
+// slice.
+#define EP_FOR_EACH_SLICE(WPB, total, wave)                                                       \
+  for (int wave = uniform((int)blockIdx.x * (WPB) + (int)(threadIdx.x >> 6)); wave < (total); \
+       wave += (int)gridDim.x * (WPB))
 
 template <int NC, int AUX_LD>
 __device__ __forceinline__ void load_row(const RowParams& p, const Slice& sl, int lane, u32x4 (&v)[NC]) {
@@ -83,11 +89,11 @@ __device__ __forceinline__ u32x4 scale8(u32x4 v, float w) {
 // NC: chunk capacity of the instantiation (>= chunks per wavefront).
 // SCALED: copy j is BF16_RNE(w[t,j] * x[t]) instead of x[t] (the output-row
 // gradients of the combine backward: a dispatch scaled per copy).
-template <int NC, int AUX_LD, int AUX_ST, bool SCALED>
-__global__ __launch_bounds__(256) void dispatch_bf16_kernel(RowParams p, int wpt, int cpw, int nchunks) {
+template <int NC, int AUX_LD, int AUX_ST, bool SCALED, int WPB>
+__global__ __launch_bounds__(64 * WPB) void dispatch_bf16_kernel(RowParams p, int wpt, int cpw, int nchunks) {
   const int lane = threadIdx.x & 63;
-  Slice sl;
-  if (!slice_of(p, wpt, cpw, nchunks, sl)) return;
+  EP_FOR_EACH_SLICE(WPB, p.T * wpt, wave) {
+  const Slice sl = slice_of(wave, wpt, cpw, nchunks);
   u32x4 v[NC];
   load_row<NC, AUX_LD>(p, sl, lane, v);
   const int slots = load_lane_slot(p.slot, sl.t, p.k, lane);
@@ -103,13 +109,20 @@ __global__ __launch_bounds__(256) void dispatch_bf16_kernel(RowParams p, int wpt
     if constexpr (SCALED) {
       const float w = __uint_as_float((uint32_t)__builtin_amdgcn_readlane(wl, j));
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        if (c < sl.nc) store16<AUX_ST>(rd, col + 1024u * c, scale8(v[c], w));
+      for (int c = 0; c < NC; ++c) {
+        // Re-widen the row for every copy: an empty asm makes the register
+        // opaque, so the compiler does not keep 8 * NC widened floats live
+        // across the j loop (which halves occupancy at NC = 14).
+        u32x4 vc = v[c];
+        asm volatile("" : "+v"(vc));
+        if (c < sl.nc) store16<AUX_ST>(rd, col + 1024u * c, scale8(vc, w));
+      }
     } else {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
         if (c < sl.nc) store16<AUX_ST>(rd, col + 1024u * c, v[c]);
     }
+  }
   }
 }
 
@@ -133,12 +146,12 @@ __device__ __forceinline__ float block_scale(uint32_t amax_bits16) {
 // even lane of a lane pair stores 16 bytes of chunk 2m, the odd lane the same
 // bytes of chunk 2m+1.  A pair whose second chunk lies past the row stores
 // that half out of range, where the store is dropped.
-template <int NC, int AUX_LD, int AUX_ST>
-__global__ __launch_bounds__(256) void dispatch_fp8_kernel(RowParams p, int wpt, int cpw, int nchunks) {
+template <int NC, int AUX_LD, int AUX_ST, int WPB>
+__global__ __launch_bounds__(64 * WPB) void dispatch_fp8_kernel(RowParams p, int wpt, int cpw, int nchunks) {
   static_assert(NC % 2 == 0, "chunks pair up");
   const int lane = threadIdx.x & 63;
-  Slice sl;
-  if (!slice_of(p, wpt, cpw, nchunks, sl)) return;
+  EP_FOR_EACH_SLICE(WPB, p.T * wpt, wave) {
+  const Slice sl = slice_of(wave, wpt, cpw, nchunks);
   u32x4 v[NC];
   load_row<NC, AUX_LD>(p, sl, lane, v);
   const int slots = load_lane_slot(p.slot, sl.t, p.k, lane);
@@ -189,7 +202,10 @@ __global__ __launch_bounds__(256) void dispatch_fp8_kernel(RowParams p, int wpt,
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(my_scale), rs, (int)scol, 0, AUX_ST);
     }
   }
+  }
 }
+
+#undef EP_FOR_EACH_SLICE
 
 __global__ __launch_bounds__(256) void check_cvt_e4m3_kernel(const float* in, uint8_t* out, int64_t n) {
   for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n;
@@ -215,24 +231,33 @@ __global__ __launch_bounds__(256) void check_cvt_bf16_kernel(const float* in, ui
   }
 }
 
-// Wavefronts per token and (even) chunks per wavefront for hidden size H.
+// Wavefronts per token, (even) chunks per wavefront and the launch shape.
 struct Split {
   int nchunks, wpt, cpw, blocks;
+  bool budget;  // persistent kBudgetWaves-wavefront workgroups, one per CU of the budget
 };
 
 Split split_for(const RowParams& p) {
   Split s;
   s.nchunks = (p.H + 511) / 512;
+  s.budget = p.num_cus > 0;
   // Whole rows per wavefront for long bursts, unless the batch is too small
-  // to give every CU a few wavefronts: then rows split into 2-chunk slices.
+  // to give every CU (or every wavefront of the budget) some work: then rows
+  // split into 2-chunk slices.
   const int min_wpt = (s.nchunks + kMaxChunks - 1) / kMaxChunks;
-  const int want_wpt = (kMinWaves + p.T - 1) / p.T;
+  const int min_waves = s.budget ? p.num_cus * kBudgetWaves : kMinWaves;
+  const int want_wpt = (min_waves + p.T - 1) / p.T;
   s.wpt = max(min_wpt, min(want_wpt, (s.nchunks + 1) / 2));
   s.cpw = (s.nchunks + s.wpt - 1) / s.wpt;
   s.cpw += s.cpw & 1;
   s.wpt = (s.nchunks + s.cpw - 1) / s.cpw;
   const int64_t waves = (int64_t)p.T * s.wpt;
-  s.blocks = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+  if (s.budget) {
+    const int64_t need = (waves + kBudgetWaves - 1) / kBudgetWaves;
+    s.blocks = (int)(need < p.num_cus ? need : p.num_cus);
+  } else {
+    s.blocks = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+  }
   return s;
 }
 
@@ -240,14 +265,22 @@ Split split_for(const RowParams& p) {
 
 namespace {
 
+template <int NC, bool SCALED, int WPB>
+void launch_bf16_ncsw(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  if (streaming)
+    hipLaunchKernelGGL((dispatch_bf16_kernel<NC, kAuxDefault, kAuxNT, SCALED, WPB>), dim3(s.blocks), dim3(64 * WPB),
+                       0, stream, p, s.wpt, s.cpw, s.nchunks);
+  else
+    hipLaunchKernelGGL((dispatch_bf16_kernel<NC, kAuxDefault, kAuxDefault, SCALED, WPB>), dim3(s.blocks),
+                       dim3(64 * WPB), 0, stream, p, s.wpt, s.cpw, s.nchunks);
+}
+
 template <int NC, bool SCALED>
 void launch_bf16_ncs(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
-  if (streaming)
-    hipLaunchKernelGGL((dispatch_bf16_kernel<NC, kAuxDefault, kAuxNT, SCALED>), dim3(s.blocks), dim3(256), 0, stream,
-                       p, s.wpt, s.cpw, s.nchunks);
+  if (s.budget)
+    launch_bf16_ncsw<NC, SCALED, kBudgetWaves>(s, p, streaming, stream);
   else
-    hipLaunchKernelGGL((dispatch_bf16_kernel<NC, kAuxDefault, kAuxDefault, SCALED>), dim3(s.blocks), dim3(256), 0,
-                       stream, p, s.wpt, s.cpw, s.nchunks);
+    launch_bf16_ncsw<NC, SCALED, kWavesPerBlock>(s, p, streaming, stream);
 }
 
 template <int NC>
@@ -258,14 +291,22 @@ void launch_bf16_nc(const Split& s, const RowParams& p, bool streaming, hipStrea
     launch_bf16_ncs<NC, false>(s, p, streaming, stream);
 }
 
+template <int NC, int WPB>
+void launch_fp8_ncw(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  if (streaming)
+    hipLaunchKernelGGL((dispatch_fp8_kernel<NC, kAuxDefault, kAuxNT, WPB>), dim3(s.blocks), dim3(64 * WPB), 0, stream,
+                       p, s.wpt, s.cpw, s.nchunks);
+  else
+    hipLaunchKernelGGL((dispatch_fp8_kernel<NC, kAuxDefault, kAuxDefault, WPB>), dim3(s.blocks), dim3(64 * WPB), 0,
+                       stream, p, s.wpt, s.cpw, s.nchunks);
+}
+
 template <int NC>
 void launch_fp8_nc(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
-  if (streaming)
-    hipLaunchKernelGGL((dispatch_fp8_kernel<NC, kAuxDefault, kAuxNT>), dim3(s.blocks), dim3(256), 0, stream, p,
-                       s.wpt, s.cpw, s.nchunks);
+  if (s.budget)
+    launch_fp8_ncw<NC, kBudgetWaves>(s, p, streaming, stream);
   else
-    hipLaunchKernelGGL((dispatch_fp8_kernel<NC, kAuxDefault, kAuxDefault>), dim3(s.blocks), dim3(256), 0, stream,
-                       p, s.wpt, s.cpw, s.nchunks);
+    launch_fp8_ncw<NC, kWavesPerBlock>(s, p, streaming, stream);
 }
 
 }  // namespace

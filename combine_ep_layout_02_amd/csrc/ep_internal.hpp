@@ -50,6 +50,7 @@ struct RowParams {
   float* recv_scale;        // FP8 dispatch only
   int T, H, k;
   int64_t rows;             // receive rows (bounds for slot values)
+  int num_cus;              // 0: whole GPU; n > 0: n persistent workgroups of kBudgetWaves wavefronts
 };
 
 // Combine backward: g [T, H] and y [rows, H] BF16, grad_y [rows, H] BF16,
@@ -63,7 +64,12 @@ struct BackParams {
   float* grad_w;
   int T, H, k;
   int64_t rows;
+  int num_cus;  // as in RowParams
 };
+
+// Wavefronts per workgroup of a launch limited to a CU budget: one 1024-thread
+// workgroup per CU of the budget.
+constexpr int kBudgetWaves = 16;
 
 // Upper bound of num_topk (the C ABI's EP_MAX_TOPK), for LDS sizing.
 constexpr int kMaxTopk = 64;

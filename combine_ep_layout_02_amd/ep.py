@@ -25,6 +25,7 @@ EP_FP8_E4M3 = 1
 EP_OK = 0
 EP_MAX_EXPERTS = 2048
 EP_MAX_TOPK = 64
+EP_MAX_NUM_CUS = 65535
 
 EXPORTED = ("ep_recv_rows", "ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_combine",
             "ep_dispatch_backward", "ep_combine_backward", "ep_status_string", "ep_abi_version",
@@ -43,12 +44,13 @@ class EpError(RuntimeError):
 
 class _Shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("num_tokens", "hidden", "num_topk", "num_experts",
-                                                "num_ranks", "expert_alignment", "capacity")]
+                                                "num_ranks", "expert_alignment", "capacity", "num_cus")]
 
 
 @dataclass(frozen=True)
 class EpShape:
-    """ep_shape_t: T tokens of hidden H routed to k of E experts in R ranks."""
+    """ep_shape_t: T tokens of hidden H routed to k of E experts in R ranks; num_cus is the
+    launch budget of dispatch / combine (0 = the whole GPU)."""
     num_tokens: int
     hidden: int
     num_topk: int
@@ -56,10 +58,11 @@ class EpShape:
     num_ranks: int
     expert_alignment: int = 1
     capacity: int = 0
+    num_cus: int = 0
 
     def c(self) -> _Shape:
         return _Shape(self.num_tokens, self.hidden, self.num_topk, self.num_experts, self.num_ranks,
-                      self.expert_alignment, self.capacity)
+                      self.expert_alignment, self.capacity, self.num_cus)
 
     @cached_property
     def c_ref(self):

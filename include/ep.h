@@ -55,11 +55,12 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 2
+#define EP_ABI_VERSION 3
 
 /* Limits checked by every entry point (EP_ERR_UNSUPPORTED beyond them). */
 #define EP_MAX_EXPERTS 2048
 #define EP_MAX_TOPK 64
+#define EP_MAX_NUM_CUS 65535
 
 /*
  * Problem shape.  T tokens of hidden size H, each routed to k experts out of
@@ -78,6 +79,17 @@ extern "C" {
  *   capacity          C >= 0: 0 = flat expert-major layout; C > 0 = padded
  *                     per-expert layout [E, C] (low-latency decode form),
  *                     requires A == 1
+ *   num_cus           launch budget of dispatch, combine and the backward
+ *                     pair, the analog of DeepEP's num_sms argument ([GN]
+ *                     "Interfaz centrada en ElasticBuffer": a caller-given
+ *                     SM count overrides the computed one).  0 = the whole
+ *                     GPU: one wavefront per work item.  n in
+ *                     [1, EP_MAX_NUM_CUS] = n persistent workgroups of up to
+ *                     1024 threads that loop over the work, which on an
+ *                     otherwise idle MI355X the dispatcher places on n
+ *                     distinct CUs, leaving the rest to kernels on other
+ *                     streams.  Results do not depend on it.  ep_layout
+ *                     ignores it (its launch is latency-bound and small).
  */
 typedef struct ep_shape_t {
     int32_t num_tokens;
@@ -87,6 +99,7 @@ typedef struct ep_shape_t {
     int32_t num_ranks;
     int32_t expert_alignment;
     int32_t capacity;
+    int32_t num_cus;
 } ep_shape_t;
 
 typedef enum ep_dtype_t {

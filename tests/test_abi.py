@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_abi_version_and_status_strings(L):
     header = open(HEADER).read()
-    assert ep.ep_abi_version() == int(re.search(r"#define EP_ABI_VERSION (\d+)", header).group(1)) == 2
+    assert ep.ep_abi_version() == int(re.search(r"#define EP_ABI_VERSION (\d+)", header).group(1)) == 3
     for code in range(6):
         s = ep.ep_status_string(code)
         assert s.startswith("EP_"), s
@@ -62,7 +62,7 @@ def test_abi_version_and_status_strings(L):
 
 def shape_c(**kw):
     base = dict(num_tokens=16, hidden=256, num_topk=2, num_experts=8, num_ranks=2, expert_alignment=1,
-                capacity=0)
+                capacity=0, num_cus=0)
     base.update(kw)
     return epmod._Shape(*[base[n] for n, _ in epmod._Shape._fields_])
 
@@ -81,6 +81,19 @@ def test_recv_rows_matches_workloads(L, name):
     assert ep.ep_layout_workspace_bytes(s) > 0
 
 
+def test_shape_struct_matches_header():
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct ep_shape_t \{(.*?)\} ep_shape_t;", src, re.S).group(1)
+    fields = re.findall(r"int32_t (\w+);", body)
+    assert fields == [n for n, _ in epmod._Shape._fields_]
+    assert "#define EP_MAX_NUM_CUS %d" % epmod.EP_MAX_NUM_CUS in open(HEADER).read()
+
+
+def test_num_cus_accepted_in_range(L):
+    assert rows_status(L, num_cus=1)[0] == OK
+    assert rows_status(L, num_cus=65535)[0] == OK
+
+
 def test_recv_rows_formula(L):
     assert rows_status(L, num_tokens=10, num_topk=3, num_experts=6, num_ranks=3, expert_alignment=4) == (OK, 30 + 18)
     assert rows_status(L, num_tokens=10, num_topk=3, num_experts=6, num_ranks=3, capacity=7) == (OK, 42)
@@ -96,6 +109,8 @@ def test_recv_rows_formula(L):
     (dict(num_experts=128, num_topk=65), UNSUPPORTED),
     (dict(num_tokens=1 << 30, num_topk=4), UNSUPPORTED),
     (dict(num_experts=2048, num_ranks=8, capacity=1 << 21), UNSUPPORTED),
+    (dict(num_cus=-1), INVALID), (dict(num_cus=65536), UNSUPPORTED),
+    (dict(num_tokens=1 << 20, hidden=1 << 20, num_topk=1), UNSUPPORTED),   # 2^31 (token, chunk) items
 ])
 def test_bad_shapes_rejected(L, kw, code):
     st, _ = rows_status(L, **kw)

@@ -85,10 +85,11 @@ extern "C" {
  *                     SM count overrides the computed one).  0 = the whole
  *                     GPU: one wavefront per work item.  n in
  *                     [1, EP_MAX_NUM_CUS] = n persistent workgroups of up to
- *                     1024 threads that loop over the work, which on an
- *                     otherwise idle MI355X the dispatcher places on n
- *                     distinct CUs, leaving the rest to kernels on other
- *                     streams.  Results do not depend on it.  ep_layout
+ *                     1024 threads that loop over the work; the hardware
+ *                     dispatcher spreads them over the CUs (on an idle
+ *                     MI355X the bandwidth grows linearly with n up to
+ *                     ~96), leaving the rest of the chip to kernels on
+ *                     other streams.  Results do not depend on it.  ep_layout
  *                     ignores it (its launch is latency-bound and small).
  */
 typedef struct ep_shape_t {

@@ -62,6 +62,14 @@ def lib():
         L.oracle_combine.argtypes = [i64, i64, i64, vp, vp, vp, vp]
         L.oracle_dispatch_backward.argtypes = [i64, i64, i64, vp, vp, vp]
         L.oracle_combine_backward.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.oracle_dispatch_prequantized.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp]
+        L.oracle_e2m1_decode.restype = ctypes.c_double
+        L.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e2m1_encode.restype = ctypes.c_uint8
+        L.oracle_e2m1_encode.argtypes = [ctypes.c_float]
+        L.oracle_mx_exponent.restype = ctypes.c_int
+        L.oracle_mx_exponent.argtypes = [ctypes.c_float, ctypes.c_int]
+        L.oracle_dispatch_mx.argtypes = [i64, i64, i64, ctypes.c_int, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -187,3 +195,45 @@ def combine_backward(grad_out: np.ndarray, y: np.ndarray, slot: np.ndarray, weig
     gw = np.zeros((T, k), np.float64)
     lib().oracle_combine_backward(T, H, k, _p(g), _p(y), _p(slot), _p(w), _p(gy), _p(gw))
     return gy, gw
+
+
+def dispatch_prequantized(x_q: np.ndarray, x_s: np.ndarray, slot: np.ndarray, rows: int):
+    """Copy the caller's E4M3 codes [T, H] and fp32 block scales [T, H/128] to every valid slot."""
+    x_q = _c(x_q, np.uint8)
+    x_s = _c(x_s, np.float32)
+    slot = _c(slot, np.int32)
+    T, H = x_q.shape
+    k = slot.shape[1]
+    q = np.zeros((rows, H), np.uint8)
+    s = np.zeros((rows, H // 128), np.float32)
+    lib().oracle_dispatch_prequantized(T, H, k, _p(x_q), _p(x_s), _p(slot), _p(q), _p(s))
+    return q, s
+
+
+def e2m1_encode(f) -> np.ndarray:
+    L = lib()
+    a = np.asarray(f, dtype=np.float32)
+    return np.array([L.oracle_e2m1_encode(float(v)) for v in a.ravel()], np.uint8).reshape(a.shape)
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    L = lib()
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([L.oracle_e2m1_decode(int(v)) for v in c.ravel()], np.float64).reshape(c.shape)
+
+
+def mx_exponent(amax: float, emax: int) -> int:
+    return int(lib().oracle_mx_exponent(float(amax), int(emax)))
+
+
+def dispatch_mx(x: np.ndarray, slot: np.ndarray, rows: int, elem_bits: int):
+    """MXFP8 (elem_bits 8) or MXFP4 (4) dispatch: codes [rows, H or H/2] and E8M0 scales [rows, H/32]."""
+    x = _c(x, np.uint16)
+    slot = _c(slot, np.int32)
+    T, H = x.shape
+    k = slot.shape[1]
+    assert H % 32 == 0 and elem_bits in (4, 8)
+    q = np.zeros((rows, H if elem_bits == 8 else H // 2), np.uint8)
+    s = np.zeros((rows, H // 32), np.uint8)
+    lib().oracle_dispatch_mx(T, H, k, elem_bits, _p(x), _p(slot), _p(q), _p(s))
+    return q, s

@@ -48,7 +48,16 @@
  *   R12 combine backward: grad_y[slot[t,j], h] = BF16_RNE(w[t,j] * g[t,h])
  *       with the product rounded to fp32 first; grad_w[t,j] = the exact dot
  *       product of g[t] and y[slot[t,j]] (returned in double); the BF16
- *       rounding of the forward output passes the gradient through as is.
+ *       rounding of the forward output passes the gradient through as is;
+ *   R13 pre-quantised dispatch: the caller's E4M3 codes and 1x128 fp32
+ *       scales are copied to every valid slot unchanged;
+ *   R14 MX dispatch (MXFP8 = E4M3 elements, MXFP4 = E2M1 elements, one
+ *       E8M0 scale per 32 columns) follows the OCP Microscaling Formats
+ *       v1.0 conversion: e = floor(log2(amax)) - emax(element), clamped to
+ *       [-127, 127] (an all-zero block takes -127), X = 2^e, element =
+ *       RNE(x / X) saturated to the element's largest normal; the scale is
+ *       stored as the biased byte e + 127; two E2M1 codes share a byte,
+ *       the even column in the low nibble.
  *
  * Build: gcc -O2 -std=c99 -ffp-contract=off -fPIC -shared oracle.c -lm
  * (no fast-math: every float operation below is one IEEE-754 binary32
@@ -428,4 +437,146 @@ void oracle_combine_backward(int64_t T, int64_t H, int64_t k,
             grad_w[t * k + j] = dot;
         }
     }
+}
+
+/* ------------------------------------------------------------------ */
+/* Other dispatch precisions                                           */
+/* ------------------------------------------------------------------ */
+/*
+ * DeepEP's dispatch also takes its FP8 input already quantised, as a
+ * (data, scale factors) pair (DeepEP documentation item 10), and the
+ * Hybrid-EP branch adds a 4-bit format (GeekNews "DeepSeek publica DeepEP
+ * ...", section "Ramas experimentales y forks de la comunidad").
+ */
+
+/*
+ * Pre-quantised FP8 dispatch (R13): every valid slot of token t receives
+ * the token's E4M3 codes x_q[t, :] and its block scales x_s[t, :] as they
+ * are (a byte copy).  x_q [T, H] bytes, x_s [T, H/128] fp32.
+ */
+void oracle_dispatch_prequantized(int64_t T, int64_t H, int64_t k,
+                                  const uint8_t *x_q, const float *x_s,
+                                  const int32_t *slot, uint8_t *recv_x,
+                                  float *recv_scale)
+{
+    int64_t t, j;
+    int64_t nb = H / 128;
+    for (t = 0; t < T; ++t)
+        for (j = 0; j < k; ++j) {
+            int32_t sl = slot[t * k + j];
+            if (sl < 0) continue;
+            memcpy(recv_x + (int64_t)sl * H, x_q + t * H, (size_t)H);
+            memcpy(recv_scale + (int64_t)sl * nb, x_s + t * nb, (size_t)nb * sizeof(float));
+        }
+}
+
+/*
+ * OCP FP4 E2M1: 1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit;
+ * magnitudes 0, 0.5 (subnormal), 1, 1.5, 2, 3, 4, 6; no Inf or NaN.
+ */
+double oracle_e2m1_decode(uint8_t c)
+{
+    int e = (c >> 1) & 3, m = c & 1;
+    double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return (c & 0x8) ? -mag : mag;
+}
+
+/*
+ * float32 -> E2M1 code (low 4 bits), nearest with ties to the even code,
+ * saturating to +-6; the sign is kept (a negative value that rounds to zero
+ * gives 0x8).  Same search as the E4M3 encoder, over the 8 magnitudes.
+ */
+uint8_t oracle_e2m1_encode(float v)
+{
+    uint8_t sign = signbit(v) ? 0x8 : 0x0;
+    double a = fabs((double)v), mid;
+    int lo = 0, hi = 7, code;
+    if (a >= 6.0) return (uint8_t)(sign | 7);
+    while (hi - lo > 1) {
+        int m = (lo + hi) / 2;
+        int below = oracle_e2m1_decode((uint8_t)m) <= a;
+        lo = below ? m : lo;
+        hi = below ? hi : m;
+    }
+    mid = 0.5 * (oracle_e2m1_decode((uint8_t)lo) + oracle_e2m1_decode((uint8_t)hi));
+    if (a < mid) code = lo;
+    else if (a > mid) code = hi;
+    else code = (lo & 1) ? hi : lo;
+    return (uint8_t)(sign | code);
+}
+
+/*
+ * MX block scale exponent (R14): e = floor(log2(amax)) - emax, clamped to
+ * [-127, 127]; amax == 0 gives -127.  emax is the element format's largest
+ * exponent: 8 for E4M3 (448 = 1.75 * 2^8), 2 for E2M1 (6 = 1.5 * 2^2).
+ * floor(log2(a)) is frexp's exponent minus one (exact for every finite a).
+ */
+int oracle_mx_exponent(float amax, int emax)
+{
+    int fe, e;
+    if (!(amax > 0.0f)) return -127;
+    (void)frexp((double)amax, &fe);   /* amax = f * 2^fe, f in [0.5, 1) */
+    e = (fe - 1) - emax;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+/*
+ * MX dispatch (R14).  elem_bits 8: MXFP8, recv_x [rows, H] E4M3 codes;
+ * elem_bits 4: MXFP4, recv_x [rows, H/2] bytes, column 2i in the low nibble
+ * of byte i.  recv_scale [rows, H/32] biased exponents (e + 127).  x / X is
+ * a division by a power of two, exact in double and in float for every
+ * BF16 x; the quotient is saturated to the element's largest normal and
+ * then rounded to the nearest element (a value at or below the largest
+ * normal never rounds past it).  H must be a multiple of 32.
+ */
+void oracle_dispatch_mx(int64_t T, int64_t H, int64_t k, int elem_bits,
+                        const uint16_t *x, const int32_t *slot,
+                        uint8_t *recv_x, uint8_t *recv_scale)
+{
+    int64_t t, b, i, j;
+    int64_t nb = H / 32;
+    int64_t row_bytes = elem_bits == 8 ? H : H / 2;
+    int emax = elem_bits == 8 ? 8 : 2;
+    double maxnorm = elem_bits == 8 ? 448.0 : 6.0;
+    uint8_t *row = (uint8_t *)malloc((size_t)(row_bytes > 0 ? row_bytes : 1));
+    uint8_t *scales = (uint8_t *)malloc((size_t)(nb > 0 ? nb : 1));
+    if (!row || !scales) { free(row); free(scales); return; }
+    for (t = 0; t < T; ++t) {
+        for (b = 0; b < nb; ++b) {
+            const uint16_t *xb = x + t * H + b * 32;
+            float amax = 0.0f;
+            int e;
+            for (i = 0; i < 32; ++i) {
+                float a = fabsf(bf16_to_f32(xb[i]));
+                if (a > amax) amax = a;
+            }
+            e = oracle_mx_exponent(amax, emax);
+            scales[b] = (uint8_t)(e + 127);
+            for (i = 0; i < 32; ++i) {
+                double q = ldexp((double)bf16_to_f32(xb[i]), -e);   /* x / 2^e, exact */
+                float qf;
+                if (q > maxnorm) q = maxnorm;
+                if (q < -maxnorm) q = -maxnorm;
+                qf = (float)q;                                       /* exact: a BF16 times 2^-e */
+                if (elem_bits == 8) {
+                    row[b * 32 + i] = oracle_e4m3_encode(qf);
+                } else {
+                    uint8_t c = oracle_e2m1_encode(qf);
+                    int64_t col = b * 32 + i;
+                    if (col % 2 == 0) row[col / 2] = c;
+                    else row[col / 2] = (uint8_t)(row[col / 2] | (c << 4));
+                }
+            }
+        }
+        for (j = 0; j < k; ++j) {
+            int32_t sl = slot[t * k + j];
+            if (sl < 0) continue;
+            memcpy(recv_x + (int64_t)sl * row_bytes, row, (size_t)row_bytes);
+            memcpy(recv_scale + (int64_t)sl * nb, scales, (size_t)nb);
+        }
+    }
+    free(row);
+    free(scales);
 }

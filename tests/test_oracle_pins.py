@@ -542,6 +542,152 @@ def test_dispatch_backward_k1_is_gather_and_within_bound():
 
 
 # --------------------------------------------------------------------------
+# other dispatch precisions: pre-quantised FP8, MXFP8, MXFP4
+# --------------------------------------------------------------------------
+
+def test_prequantized_dispatch_composes_to_fp8_dispatch():
+    """Quantising each token once (an FP8 dispatch to rows 0..T-1) and passing the
+    codes and scales through equals the fused FP8 dispatch, bit for bit."""
+    w = wl.WORKLOADS["tiny"]
+    inp = wl.make_inputs(w, with_y=False)
+    lay = oracle.layout(inp.topk_idx, w.num_experts, w.num_ranks)
+    T = w.num_tokens
+    xq, xs = oracle.dispatch_fp8(inp.x, np.arange(T, dtype=np.int32)[:, None], T)
+    got_q, got_s = oracle.dispatch_prequantized(xq, xs, lay.slot, w.recv_rows)
+    want_q, want_s = oracle.dispatch_fp8(inp.x, lay.slot, w.recv_rows)
+    assert np.array_equal(got_q, want_q) and np.array_equal(got_s, want_s)
+
+
+def test_prequantized_dispatch_copies_arbitrary_bytes():
+    rng = np.random.default_rng(21)
+    T, H, k, E = 20, 256, 3, 8
+    lay = oracle.layout(_random_idx(rng, T, k, E, mask_frac=0.2), E, 2)
+    xq = rng.integers(0, 256, (T, H), dtype=np.uint8)
+    xs = rng.standard_normal((T, H // 128)).astype(np.float32)
+    q, s = oracle.dispatch_prequantized(xq, xs, lay.slot, oracle.recv_rows(T, k, E))
+    for t in range(T):
+        for j in range(k):
+            r = lay.slot[t, j]
+            if r >= 0:
+                assert np.array_equal(q[r], xq[t]) and np.array_equal(s[r], xs[t])
+    unused = np.setdiff1d(np.arange(len(q)), lay.slot[lay.slot >= 0])
+    assert (q[unused] == 0).all()
+
+
+def test_mx_dispatch_hand_fixture():
+    g = _golden("mx_block_hand.json")
+    x = wl.f32_to_bf16_bits(np.array(g["x"], np.float32))
+    one = np.array([[0]], np.int32)
+    q8, s8 = oracle.dispatch_mx(x, one, 1, 8)
+    q4, s4 = oracle.dispatch_mx(x, one, 1, 4)
+    h8, h4 = g["mxfp8_codes_head"], g["mxfp4_bytes_head"]
+    assert q8[0, :6].tolist() == [int(c, 16) for c in h8[0]]
+    assert q8[0, 32:35].tolist() == [int(c, 16) for c in h8[1]]
+    assert (q8[0, 6:32] == 0).all() and (q8[0, 35:] == 0).all()
+    assert s8[0].tolist() == g["mxfp8_scales"]
+    assert q4[0, :3].tolist() == [int(c, 16) for c in h4[0]]
+    assert q4[0, 16:18].tolist() == [int(c, 16) for c in h4[1]]
+    assert (q4[0, 3:16] == 0).all() and (q4[0, 18:] == 0).all()
+    assert s4[0].tolist() == g["mxfp4_scales"]
+
+
+def test_e2m1_decode_table_and_roundtrip():
+    mags = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    assert oracle.e2m1_decode(np.arange(8)).tolist() == mags
+    assert oracle.e2m1_decode(np.arange(8, 16)).tolist() == [-m for m in mags]
+    assert oracle.e2m1_encode(oracle.e2m1_decode(np.arange(16))).tolist() == list(range(16))
+
+
+def test_e2m1_encode_brute_force_nearest():
+    """Nearest E2M1 magnitude in exact rationals, ties to the even code, saturating at 6,
+    over every midpoint and its float32 neighbours plus a dense grid."""
+    mags = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4),
+            Fraction(6)]
+    probes = set(np.linspace(-8, 8, 4001, dtype=np.float32).tolist())
+    for a, b in zip(mags, mags[1:]):
+        m = np.float32(float((a + b) / 2))
+        for v in (m, np.nextafter(m, np.float32(0)), np.nextafter(m, np.float32(10))):
+            probes.update([float(v), -float(v)])
+    probes.update([6.0, 6.5, 1e9, -1e9, 1e-30, -1e-30, 0.0, -0.0])
+    vals = np.array(sorted(probes), np.float32)
+    got = oracle.e2m1_encode(vals)
+    for v, c in zip(vals.tolist(), got.tolist()):
+        a = abs(Fraction(v))
+        if a >= 6:
+            want = 7
+        else:
+            d = [abs(a - m) for m in mags]
+            best = min(d)
+            cands = [i for i, x in enumerate(d) if x == best]
+            want = cands[0] if len(cands) == 1 else [i for i in cands if i % 2 == 0][0]
+        want |= 0x8 if np.signbit(np.float32(v)) else 0
+        assert c == want, (v, c, want)
+
+
+def test_mx_exponent_definition_and_e8m0_meaning():
+    """2^(e + emax) <= amax < 2^(e + emax + 1) wherever e is not clamped; clamps at -127 / 127;
+    the stored byte e + 127 decodes (torch float8_e8m0fnu) to 2^e."""
+    rng = np.random.default_rng(22)
+    vals = np.concatenate([np.float32(2.0) ** rng.integers(-149, 128, 300).astype(np.float32),
+                           rng.standard_normal(300).astype(np.float32) * np.float32(100),
+                           np.array([1.0, 3.0, 448.0, 512.0, 6.0, 7.9, 2.0 ** -126, 2.0 ** -133], np.float32)])
+    for emax in (8, 2):
+        for a in np.abs(vals):
+            if a == 0:
+                continue
+            e = oracle.mx_exponent(float(a), emax)
+            fa = Fraction(float(a))
+            if -127 < e < 127:
+                assert Fraction(2) ** (e + emax) <= fa < Fraction(2) ** (e + emax + 1)
+            elif e == -127:
+                assert fa < Fraction(2) ** (-127 + emax + 1)
+            else:
+                assert fa >= Fraction(2) ** (127 + emax)
+        assert oracle.mx_exponent(0.0, emax) == -127
+    b = np.array([0, 1, 120, 127, 133, 254], np.uint8)
+    dec = torch.from_numpy(b).view(torch.float8_e8m0fnu).float().numpy().astype(np.float64)
+    assert dec.tolist() == [2.0 ** (int(v) - 127) for v in b]
+
+
+@pytest.mark.parametrize("elem_bits", [8, 4])
+def test_mx_dispatch_error_bound_packing_and_copies(elem_bits):
+    """Per element: |x - dec(q) * 2^e| <= half an element ulp * 2^e, or x is beyond the
+    largest normal and q is the saturated code; every block's amax lands in the top
+    binade or saturates; all copies of a token are identical."""
+    w = wl.WORKLOADS["tiny"]
+    inp = wl.make_inputs(w, with_y=False)
+    lay = oracle.layout(inp.topk_idx, w.num_experts, w.num_ranks)
+    q, s = oracle.dispatch_mx(inp.x, lay.slot, w.recv_rows, elem_bits)
+    T, H = inp.x.shape
+    xf = wl.bf16_bits_to_f32(inp.x).astype(np.float64)
+    emax, maxnorm, mbits = (8, 448.0, 3) if elem_bits == 8 else (2, 6.0, 1)
+    for t in range(T):
+        rows = lay.slot[t][lay.slot[t] >= 0]
+        for r in rows[1:]:
+            assert np.array_equal(q[r], q[rows[0]]) and np.array_equal(s[r], s[rows[0]])
+        r = rows[0]
+        if elem_bits == 8:
+            codes = q[r]
+            dec = oracle.e4m3_decode(codes)
+        else:
+            codes = np.empty(H, np.uint8)
+            codes[0::2], codes[1::2] = q[r] & 0xF, q[r] >> 4
+            dec = oracle.e2m1_decode(codes)
+        e = s[r].astype(np.int64) - 127
+        X = np.repeat(np.ldexp(1.0, e), 32)
+        qv = xf[t] / X
+        # half an ulp of the element format at |q| (subnormal spacing below the min normal)
+        min_norm_exp = -6 if elem_bits == 8 else 0
+        ex = np.maximum(np.floor(np.log2(np.maximum(np.abs(qv), 1e-300))), min_norm_exp)
+        half_ulp = np.ldexp(1.0, (ex - mbits - 1).astype(np.int64))
+        sat = np.abs(qv) > maxnorm
+        assert (np.abs(qv - dec)[~sat] <= half_ulp[~sat]).all()
+        assert (np.abs(dec[sat]) == maxnorm).all() and (np.sign(dec[sat]) == np.sign(qv[sat])).all()
+        amax = np.abs(qv).reshape(-1, 32).max(1)
+        assert ((amax >= 2.0 ** emax) | (e == -127)).all() and (amax < 2.0 ** (emax + 1)).all()
+
+
+# --------------------------------------------------------------------------
 # generators
 # --------------------------------------------------------------------------
 

@@ -14,7 +14,8 @@ call in a second timed loop (mean, median, p10, p90), the roofline of the
 dominant kernel (combine, HBM-bound), the same step "cold" (each step after
 reading a 1 GiB buffer, so no cache holds its data), the decode-shaped
 workload's microseconds per call, the backward pair's kernel times on the
-same handle, warm and cold step times of the tiny, mid
+same handle, dispatch in every receive format (BF16, FP8, MXFP8, MXFP4,
+pre-quantised FP8), warm and cold step times of the tiny, mid
 and 16K-token skewed workloads, a plain 1 GiB copy as the practical
 bandwidth ceiling, and the CPU oracle timed on this host (one thread) on the
 same workload.
@@ -77,6 +78,17 @@ def bytes_dispatch(w, fp8):
     if fp8:
         return 2 * T * H + 4 * T * k + T * k * H + 4 * T * k * (H // 128)
     return 2 * T * H + 4 * T * k + 2 * T * k * H
+
+
+def bytes_dispatch_format(w, fmt):
+    """Algorithmic bytes of one dispatch call in each receive format."""
+    T, H, k = w.num_tokens, w.hidden, w.num_topk
+    base = 2 * T * H + 4 * T * k                       # read x and the slots
+    return base + {"bf16": 2 * T * k * H,
+                   "fp8": T * k * H + 4 * T * k * (H // 128),
+                   "mxfp8": T * k * H + T * k * (H // 32),
+                   "mxfp4": T * k * H // 2 + T * k * (H // 32),
+                   "fp8_prequantized": T * k * H + 4 * T * k * (H // 128) - T * H + 4 * T * (H // 128)}[fmt]
 
 
 def bytes_combine(w):
@@ -320,6 +332,45 @@ def cu_sweep(dev, budgets, gemm_n=4096, reps=10):
                     "(GEMMs alone + pairs alone) / (both streams together)"}
 
 
+def time_formats(step, reps):
+    """Dispatch of the step's tokens in every receive format, on its handle."""
+    w, dev = step.w, step.x.device
+    stream = torch.cuda.current_stream(dev)
+    shape = step.shape
+    T, H = w.num_tokens, w.hidden
+    calls = {}
+    for fmt, dt in (("bf16", ep.EP_BF16), ("fp8", ep.EP_FP8_E4M3), ("mxfp8", ep.EP_MXFP8_E4M3),
+                    ("mxfp4", ep.EP_MXFP4_E2M1)):
+        rx, rs = ep.alloc_recv(shape, dt, dev)
+        calls[fmt] = ep.prepare_dispatch(shape, step.x, step.lay.slot, dt, rx, rs, stream)
+    xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+    xs = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
+    ident = ep.EpShape(T, H, 1, w.num_experts, w.num_ranks)
+    ep.ep_dispatch(ident, step.x, torch.arange(T, dtype=torch.int32, device=dev)[:, None], ep.EP_FP8_E4M3, xq, xs)
+    rq, rs = ep.alloc_recv(shape, ep.EP_FP8_E4M3, dev)
+    calls["fp8_prequantized"] = ep.prepare_dispatch_prequantized(shape, xq, xs, step.lay.slot, rq, rs, stream)
+    out = {}
+    for fmt, fn in calls.items():
+        for _ in range(3):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+        nbytes = bytes_dispatch_format(w, fmt)
+        out[fmt] = {"us": round(us, 2), "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1)}
+    del calls
+    torch.cuda.empty_cache()
+    out["note"] = (f"dispatch of the {w.num_tokens}-token batch on the step's handle, median of {reps} calls; "
+                   "mxfp8/mxfp4 carry one E8M0 scale per 32 columns, fp8 one fp32 scale per 128; "
+                   "fp8_prequantized scatters caller-quantised codes and scales")
+    return out
+
+
 def pct(a, q):
     return round(float(np.percentile(a, q)) * 1e3, 2)
 
@@ -488,6 +539,8 @@ def main():
 
     log("[bench] backward pair")
     backward = time_backward(step, 20)
+    log("[bench] dispatch formats")
+    formats = time_formats(step, 20)
 
     dec = None
     if not args.no_decode:
@@ -561,6 +614,7 @@ def main():
                          "step_frac_of_copy": round(value / copy_gbps, 4)},
         "decode": dec,
         "backward": backward,
+        "dispatch_formats": formats,
         "configs": configs,
         "cpu_baseline": cb,
         "wall_s_timed": round(wall, 4),

@@ -125,15 +125,17 @@ EP_EXPORT ep_status_t ep_layout(const ep_shape_t* shape, const int32_t* topk_idx
 }
 
 EP_EXPORT ep_status_t ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t* slot,
-                                  ep_dtype_t recv_dtype, void* recv_x, float* recv_scale, hipStream_t stream) {
+                                  ep_dtype_t recv_dtype, void* recv_x, void* recv_scale, hipStream_t stream) {
   const ep_status_t st = check_shape(shape);
   if (st != EP_OK) return st;
-  if (recv_dtype != EP_BF16 && recv_dtype != EP_FP8_E4M3) return EP_ERR_INVALID_ARG;
+  const bool mx = recv_dtype == EP_MXFP8_E4M3 || recv_dtype == EP_MXFP4_E2M1;
+  if (recv_dtype != EP_BF16 && recv_dtype != EP_FP8_E4M3 && !mx) return EP_ERR_INVALID_ARG;
   if (recv_dtype == EP_FP8_E4M3 && shape->hidden % 128 != 0) return EP_ERR_UNSUPPORTED;
+  if (mx && shape->hidden % 32 != 0) return EP_ERR_UNSUPPORTED;
   const int T = shape->num_tokens;
   if (T == 0) return EP_OK;
   if (!x || !slot || !recv_x) return EP_ERR_INVALID_ARG;
-  if (recv_dtype == EP_FP8_E4M3 && !recv_scale) return EP_ERR_INVALID_ARG;
+  if (recv_dtype != EP_BF16 && !recv_scale) return EP_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(slot, 4) || !aligned(recv_scale, 4))
     return EP_ERR_MISALIGNED;
   ep::RowParams p{};
@@ -146,8 +148,38 @@ EP_EXPORT ep_status_t ep_dispatch(const ep_shape_t* shape, const void* x, const 
   p.k = shape->num_topk;
   p.rows = recv_rows_of(shape);
   p.num_cus = shape->num_cus;
-  return hip_status(recv_dtype == EP_BF16 ? ep::launch_dispatch_bf16(p, stream)
-                                          : ep::launch_dispatch_fp8(p, stream));
+  switch (recv_dtype) {
+    case EP_BF16: return hip_status(ep::launch_dispatch_bf16(p, stream));
+    case EP_FP8_E4M3: return hip_status(ep::launch_dispatch_fp8(p, stream));
+    case EP_MXFP8_E4M3: return hip_status(ep::launch_dispatch_mx(p, 8, stream));
+    default: return hip_status(ep::launch_dispatch_mx(p, 4, stream));
+  }
+}
+
+EP_EXPORT ep_status_t ep_dispatch_prequantized(const ep_shape_t* shape, const void* x_q, const float* x_scale,
+                                               const int32_t* slot, void* recv_x, float* recv_scale,
+                                               hipStream_t stream) {
+  const ep_status_t st = check_shape(shape);
+  if (st != EP_OK) return st;
+  if (shape->hidden % 128 != 0) return EP_ERR_UNSUPPORTED;
+  const int T = shape->num_tokens;
+  if (T == 0) return EP_OK;
+  if (!x_q || !x_scale || !slot || !recv_x || !recv_scale) return EP_ERR_INVALID_ARG;
+  if (!aligned(x_q, 16) || !aligned(recv_x, 16) || !aligned(x_scale, 4) || !aligned(slot, 4) ||
+      !aligned(recv_scale, 4))
+    return EP_ERR_MISALIGNED;
+  ep::RowParams p{};
+  p.src = x_q;
+  p.src_scale = x_scale;
+  p.slot = slot;
+  p.dst = recv_x;
+  p.recv_scale = recv_scale;
+  p.T = T;
+  p.H = shape->hidden;
+  p.k = shape->num_topk;
+  p.rows = recv_rows_of(shape);
+  p.num_cus = shape->num_cus;
+  return hip_status(ep::launch_dispatch_prequantized(p, stream));
 }
 
 EP_EXPORT ep_status_t ep_combine(const ep_shape_t* shape, const void* y, const int32_t* slot,
@@ -225,6 +257,13 @@ EP_EXPORT ep_status_t ep_check_cvt_e4m3(const float* in, uint8_t* out, int64_t n
   if (n > 0 && (!in || !out)) return EP_ERR_INVALID_ARG;
   if (!aligned(in, 4)) return EP_ERR_MISALIGNED;
   return hip_status(ep::launch_check_cvt_e4m3(in, out, n, stream));
+}
+
+EP_EXPORT ep_status_t ep_check_cvt_e2m1(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
+  if (n < 0) return EP_ERR_INVALID_ARG;
+  if (n > 0 && (!in || !out)) return EP_ERR_INVALID_ARG;
+  if (!aligned(in, 4)) return EP_ERR_MISALIGNED;
+  return hip_status(ep::launch_check_cvt_e2m1(in, out, n, stream));
 }
 
 EP_EXPORT ep_status_t ep_check_cvt_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream) {

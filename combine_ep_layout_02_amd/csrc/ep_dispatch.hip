@@ -198,8 +198,186 @@ __global__ __launch_bounds__(64 * WPB) void dispatch_fp8_kernel(RowParams p, int
     for (int m = 0; m < NC / 2; ++m)
       if (2 * m < sl.nc) store16<AUX_ST>(rd, ocol + 1024u * m, out[m]);
     if (lane < 4 * sl.nc) {
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.recv_scale + (int64_t)s * nb, (uint32_t)nb * 4u);
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(static_cast<float*>(p.recv_scale) + (int64_t)s * nb, (uint32_t)nb * 4u);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(my_scale), rs, (int)scol, 0, AUX_ST);
+    }
+  }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MX dispatch: OCP Microscaling blocks of 32 columns with one E8M0 scale.
+// The 4-bit dispatch of DeepEP's Hybrid-EP branch (GeekNews "DeepSeek publica
+// DeepEP ...", section "Ramas experimentales y forks de la comunidad") maps
+// on MI355X to the MX formats its matrix cores read natively.  Per block:
+// e = floor(log2 amax) - emax (clamped to [-127, 127]; an all-zero block gets
+// -127), element = RNE(x * 2^-e) saturated to the element's largest normal,
+// stored scale byte e + 127.  MXFP8 elements are E4M3 (emax 8), MXFP4 E2M1
+// (emax 2, two per byte, the even column in the low nibble).
+//
+// A 32-column block is one lane quad (8 columns per lane), so the block amax
+// is two DPP max steps.  For a BF16 amax with biased exponent E,
+// floor(log2 amax) = E - 127 (E = 0, zero or subnormal, clamps to -127), so
+// the scale byte is max(E - emax, 0) and 2^-e is built from its exponent
+// bits; x * 2^-e is exact.
+// ---------------------------------------------------------------------------
+
+// E2M1 code of v (4 bits), nearest with ties to the even code, saturating at
+// 6, sign kept.  The magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 are codes 0..7, so
+// the code is the number of rounding thresholds |v| has passed; a threshold
+// that is a tie counts as passed only when the upper code is even.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float m = fabsf(v);
+  const uint32_t c = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
+                     (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) + (uint32_t)(m > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 0x8u);
+}
+
+// Maximum over each lane quad (one 32-column MX block).
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  return v;
+}
+
+template <int ELEM>
+struct MxFormat;
+template <>
+struct MxFormat<8> {
+  static constexpr int kEmax = 8;
+  static constexpr float kMaxNorm = 448.0f;
+};
+template <>
+struct MxFormat<4> {
+  static constexpr int kEmax = 2;
+  static constexpr float kMaxNorm = 6.0f;
+};
+
+// ELEM 8: 8 E4M3 codes per lane and chunk (8 bytes); ELEM 4: 8 E2M1 codes
+// (4 bytes).  The 16 scale bytes of a chunk are gathered into 4 dwords, and
+// lane L < 4 * nc holds dword L % 4 of chunk L / 4, so one store per receive
+// row writes the slice's scales as one contiguous run.
+template <int NC, int AUX_LD, int AUX_ST, int WPB, int ELEM>
+__global__ __launch_bounds__(64 * WPB) void dispatch_mx_kernel(RowParams p, int wpt, int cpw, int nchunks) {
+  using F = MxFormat<ELEM>;
+  const int lane = threadIdx.x & 63;
+  EP_FOR_EACH_SLICE(WPB, p.T * wpt, wave) {
+  const Slice sl = slice_of(wave, wpt, cpw, nchunks);
+  u32x4 v[NC];
+  load_row<NC, AUX_LD>(p, sl, lane, v);
+  const int slots = load_lane_slot(p.slot, sl.t, p.k, lane);
+
+  uint32_t code[NC][ELEM == 8 ? 2 : 1];
+  uint32_t sdw[NC];  // scale dword of lanes 0, 16, 32, 48: quads 4r .. 4r+3 of the chunk
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const uint32_t E = quad_max_u32(absmax_bits8(v[c])) >> 7;           // biased exponent of the block amax
+    const uint32_t sbyte = E > (uint32_t)F::kEmax ? E - F::kEmax : 0u;  // e + 127
+    const float inv = __uint_as_float((254u - sbyte) << 23);             // 2^-e
+    float q[8];
+    q[0] = bf16_lo(v[c].x) * inv; q[1] = bf16_hi(v[c].x) * inv;
+    q[2] = bf16_lo(v[c].y) * inv; q[3] = bf16_hi(v[c].y) * inv;
+    q[4] = bf16_lo(v[c].z) * inv; q[5] = bf16_hi(v[c].z) * inv;
+    q[6] = bf16_lo(v[c].w) * inv; q[7] = bf16_hi(v[c].w) * inv;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(q[i], -F::kMaxNorm), F::kMaxNorm);
+    if constexpr (ELEM == 8) {
+      code[c][0] = pack_e4m3x4(q[0], q[1], q[2], q[3]);
+      code[c][1] = pack_e4m3x4(q[4], q[5], q[6], q[7]);
+    } else {
+      uint32_t w = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w |= e2m1_code(q[i]) << (4 * i);
+      code[c][0] = w;
+    }
+    // scale bytes of quads 4r..4r+3 into lane 16r (every lane of a quad holds its byte)
+    const uint32_t b1 = (uint32_t)__shfl((int)sbyte, lane + 4, 64);
+    const uint32_t b2 = (uint32_t)__shfl((int)sbyte, lane + 8, 64);
+    const uint32_t b3 = (uint32_t)__shfl((int)sbyte, lane + 12, 64);
+    sdw[c] = sbyte | (b1 << 8) | (b2 << 16) | (b3 << 24);
+  }
+  uint32_t my_sdw = 0;
+  const int owner = (lane & 3) << 4;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const uint32_t g = (uint32_t)__shfl((int)sdw[c], owner, 64);
+    if ((lane >> 2) == c) my_sdw = g;
+  }
+
+  const int H = p.H, nb = H >> 5;
+  const uint32_t row_bytes = ELEM == 8 ? (uint32_t)H : (uint32_t)H / 2u;
+  const uint32_t ocol = (uint32_t)(sl.c0 * 512 + lane * 8) * (uint32_t)ELEM / 8u;
+  const uint32_t chunk_bytes = 512u * (uint32_t)ELEM / 8u;
+  const uint32_t scol = (uint32_t)(sl.c0 * 16 + lane * 4);
+  uint8_t* dst = static_cast<uint8_t*>(p.dst);
+  uint8_t* sdst = static_cast<uint8_t*>(p.recv_scale);
+  for (int j = 0; j < p.k; ++j) {
+    const int s = __builtin_amdgcn_readlane(slots, j);
+    if (!slot_ok(s, p.rows)) continue;
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dst + (int64_t)s * row_bytes, row_bytes);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (c >= sl.nc) continue;
+      if constexpr (ELEM == 8) {
+        u32x2 w2 = {code[c][0], code[c][1]};
+        store8<AUX_ST>(rd, ocol + chunk_bytes * c, w2);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b32(code[c][0], rd, (int)(ocol + chunk_bytes * c), 0, AUX_ST);
+      }
+    }
+    if (lane < 4 * sl.nc) {
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(sdst + (int64_t)s * nb, (uint32_t)nb);
+      __builtin_amdgcn_raw_buffer_store_b32(my_sdw, rs, (int)scol, 0, AUX_ST);
+    }
+  }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pre-quantised FP8 dispatch: DeepEP's dispatch also takes FP8 input as a
+// (data, scale factors) pair (DeepEP documentation item 10).  The caller's
+// E4M3 codes [T, H] and fp32 scales [T, H/128] go to every valid slot as
+// they are: a byte scatter.  The launch treats a code row as H/2 two-byte
+// columns, so a 512-column chunk here is 1024 code bytes (16 per lane) and
+// carries 8 block scales.
+// ---------------------------------------------------------------------------
+template <int NC, int AUX_LD, int AUX_ST, int WPB>
+__global__ __launch_bounds__(64 * WPB) void dispatch_prequantized_kernel(RowParams p, int wpt, int cpw,
+                                                                         int nchunks) {
+  const int lane = threadIdx.x & 63;
+  EP_FOR_EACH_SLICE(WPB, p.T * wpt, wave) {
+  const Slice sl = slice_of(wave, wpt, cpw, nchunks);
+  u32x4 v[NC];
+  load_row<NC, AUX_LD>(p, sl, lane, v);  // p.H counts two-byte columns
+  const int slots = load_lane_slot(p.slot, sl.t, p.k, lane);
+  const int nb = p.H >> 6;               // scales per row: (2 H) / 128
+  const int sc0 = sl.c0 * 8, nsc = min(8 * sl.nc, nb - sc0);
+  // lane L holds scales sc0 + L and sc0 + 64 + L of the slice (8 per chunk)
+  const __amdgpu_buffer_rsrc_t rsi = make_rsrc(p.src_scale + (int64_t)sl.t * nb, (uint32_t)nb * 4u);
+  uint32_t scale[NC > 8 ? 2 : 1];
+#pragma unroll
+  for (int m = 0; m < (NC > 8 ? 2 : 1); ++m) {
+    const int i = 64 * m + lane;
+    scale[m] = __builtin_amdgcn_raw_buffer_load_b32(rsi, i < nsc ? (int)((sc0 + i) * 4) : (int)kNoColumn, 0, 0);
+  }
+
+  uint8_t* dst = static_cast<uint8_t*>(p.dst);
+  float* sdst = static_cast<float*>(p.recv_scale);
+  const uint32_t row_bytes = (uint32_t)p.H * 2u;
+  const uint32_t col = (uint32_t)(sl.c0 * 512 + lane * 8) * 2u;
+  for (int j = 0; j < p.k; ++j) {
+    const int s = __builtin_amdgcn_readlane(slots, j);
+    if (!slot_ok(s, p.rows)) continue;
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dst + (int64_t)s * row_bytes, row_bytes);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      if (c < sl.nc) store16<AUX_ST>(rd, col + 1024u * c, v[c]);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sdst + (int64_t)s * nb, (uint32_t)nb * 4u);
+#pragma unroll
+    for (int m = 0; m < (NC > 8 ? 2 : 1); ++m) {
+      const int i = 64 * m + lane;
+      if (i < nsc) __builtin_amdgcn_raw_buffer_store_b32(scale[m], rs, (sc0 + i) * 4, 0, AUX_ST);
     }
   }
   }
@@ -218,6 +396,11 @@ __global__ __launch_bounds__(256) void check_cvt_e4m3_kernel(const float* in, ui
     for (int m = 0; m < 4; ++m)
       if (i + m < n) out[i + m] = (uint8_t)(q >> (8 * m));
   }
+}
+
+__global__ __launch_bounds__(256) void check_cvt_e2m1_kernel(const float* in, uint8_t* out, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = (uint8_t)e2m1_code(in[i]);
 }
 
 __global__ __launch_bounds__(256) void check_cvt_bf16_kernel(const float* in, uint16_t* out, int64_t n) {
@@ -301,6 +484,52 @@ void launch_fp8_ncw(const Split& s, const RowParams& p, bool streaming, hipStrea
                        stream, p, s.wpt, s.cpw, s.nchunks);
 }
 
+template <int NC, int WPB, int ELEM>
+void launch_mx_ncw(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  if (streaming)
+    hipLaunchKernelGGL((dispatch_mx_kernel<NC, kAuxDefault, kAuxNT, WPB, ELEM>), dim3(s.blocks), dim3(64 * WPB), 0,
+                       stream, p, s.wpt, s.cpw, s.nchunks);
+  else
+    hipLaunchKernelGGL((dispatch_mx_kernel<NC, kAuxDefault, kAuxDefault, WPB, ELEM>), dim3(s.blocks),
+                       dim3(64 * WPB), 0, stream, p, s.wpt, s.cpw, s.nchunks);
+}
+
+template <int NC, int ELEM>
+void launch_mx_nce(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  if (s.budget)
+    launch_mx_ncw<NC, kBudgetWaves, ELEM>(s, p, streaming, stream);
+  else
+    launch_mx_ncw<NC, kWavesPerBlock, ELEM>(s, p, streaming, stream);
+}
+
+template <int NC>
+void launch_mx8_nc(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  launch_mx_nce<NC, 8>(s, p, streaming, stream);
+}
+
+template <int NC>
+void launch_mx4_nc(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  launch_mx_nce<NC, 4>(s, p, streaming, stream);
+}
+
+template <int NC, int WPB>
+void launch_pq_ncw(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  if (streaming)
+    hipLaunchKernelGGL((dispatch_prequantized_kernel<NC, kAuxDefault, kAuxNT, WPB>), dim3(s.blocks), dim3(64 * WPB),
+                       0, stream, p, s.wpt, s.cpw, s.nchunks);
+  else
+    hipLaunchKernelGGL((dispatch_prequantized_kernel<NC, kAuxDefault, kAuxDefault, WPB>), dim3(s.blocks),
+                       dim3(64 * WPB), 0, stream, p, s.wpt, s.cpw, s.nchunks);
+}
+
+template <int NC>
+void launch_pq_nc(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  if (s.budget)
+    launch_pq_ncw<NC, kBudgetWaves>(s, p, streaming, stream);
+  else
+    launch_pq_ncw<NC, kWavesPerBlock>(s, p, streaming, stream);
+}
+
 template <int NC>
 void launch_fp8_nc(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
   if (s.budget)
@@ -341,6 +570,28 @@ hipError_t launch_dispatch_fp8(const RowParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t launch_dispatch_mx(const RowParams& p, int elem_bits, hipStream_t stream) {
+  if (p.T == 0) return hipSuccess;
+  const Split s = split_for(p);
+  const bool streaming = (int64_t)p.T * p.k * p.H * elem_bits / 8 >= kStreamingBytes;
+  if (elem_bits == 8) {
+    EP_BY_CAPACITY(launch_mx8_nc, s, p, streaming, stream);
+  } else {
+    EP_BY_CAPACITY(launch_mx4_nc, s, p, streaming, stream);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_prequantized(const RowParams& p_in, hipStream_t stream) {
+  if (p_in.T == 0) return hipSuccess;
+  RowParams p = p_in;
+  p.H = p_in.H / 2;  // code rows as two-byte columns
+  const Split s = split_for(p);
+  const bool streaming = (int64_t)p.T * p.k * p_in.H >= kStreamingBytes;
+  EP_BY_CAPACITY(launch_pq_nc, s, p, streaming, stream);
+  return hipGetLastError();
+}
+
 #undef EP_BY_CAPACITY
 
 hipError_t launch_check_cvt_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
@@ -348,6 +599,14 @@ hipError_t launch_check_cvt_e4m3(const float* in, uint8_t* out, int64_t n, hipSt
   const int64_t want = (n + 1023) / 1024;
   const int blocks = (int)(want < 65536 ? want : 65536);
   hipLaunchKernelGGL(check_cvt_e4m3_kernel, dim3(blocks), dim3(256), 0, stream, in, out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_cvt_e2m1(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t want = (n + 255) / 256;
+  const int blocks = (int)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(check_cvt_e2m1_kernel, dim3(blocks), dim3(256), 0, stream, in, out, n);
   return hipGetLastError();
 }
 

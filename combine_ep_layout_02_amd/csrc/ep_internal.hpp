@@ -47,7 +47,8 @@ struct RowParams {
   const float* weights;     // combine: null = every weight 1 (dispatch backward);
                             // BF16 dispatch: non-null = copy j scaled by w[t,j] (combine backward)
   void* dst;                // recv_x (dispatch) or out (combine)
-  float* recv_scale;        // FP8 dispatch only
+  void* recv_scale;         // FP8: fp32 [rows, H/128]; MX: E8M0 bytes [rows, H/32]
+  const float* src_scale;   // pre-quantised dispatch: the caller's fp32 scales [T, H/128]
   int T, H, k;
   int64_t rows;             // receive rows (bounds for slot values)
   int num_cus;              // 0: whole GPU; n > 0: n persistent workgroups of kBudgetWaves wavefronts
@@ -76,10 +77,13 @@ constexpr int kMaxTopk = 64;
 
 hipError_t launch_dispatch_bf16(const RowParams& p, hipStream_t stream);  // weights non-null: scaled copies
 hipError_t launch_dispatch_fp8(const RowParams& p, hipStream_t stream);
+hipError_t launch_dispatch_mx(const RowParams& p, int elem_bits, hipStream_t stream);  // 8: MXFP8, 4: MXFP4
+hipError_t launch_dispatch_prequantized(const RowParams& p, hipStream_t stream);     // src = E4M3 codes
 hipError_t launch_combine(const RowParams& p, hipStream_t stream);  // weights null: unit weights
 hipError_t launch_combine_backward(const BackParams& p, hipStream_t stream);
 
 hipError_t launch_check_cvt_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 hipError_t launch_check_cvt_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream);
+hipError_t launch_check_cvt_e2m1(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 
 }  // namespace ep

@@ -22,14 +22,16 @@ _lib = None
 
 EP_BF16 = 0
 EP_FP8_E4M3 = 1
+EP_MXFP8_E4M3 = 2
+EP_MXFP4_E2M1 = 3
 EP_OK = 0
 EP_MAX_EXPERTS = 2048
 EP_MAX_TOPK = 64
 EP_MAX_NUM_CUS = 65535
 
-EXPORTED = ("ep_recv_rows", "ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_combine",
-            "ep_dispatch_backward", "ep_combine_backward", "ep_status_string", "ep_abi_version",
-            "ep_last_hip_error", "ep_check_cvt_e4m3", "ep_check_cvt_bf16")
+EXPORTED = ("ep_recv_rows", "ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_dispatch_prequantized",
+            "ep_combine", "ep_dispatch_backward", "ep_combine_backward", "ep_status_string", "ep_abi_version",
+            "ep_last_hip_error", "ep_check_cvt_e4m3", "ep_check_cvt_bf16", "ep_check_cvt_e2m1")
 
 
 class EpError(RuntimeError):
@@ -105,6 +107,8 @@ def lib() -> ctypes.CDLL:
         L.ep_layout.argtypes = [sp] + [vp] * 9 + [ctypes.c_size_t, vp]
         L.ep_dispatch.restype = st
         L.ep_dispatch.argtypes = [sp, vp, vp, ctypes.c_int, vp, vp, vp]
+        L.ep_dispatch_prequantized.restype = st
+        L.ep_dispatch_prequantized.argtypes = [sp, vp, vp, vp, vp, vp, vp]
         L.ep_combine.restype = st
         L.ep_combine.argtypes = [sp, vp, vp, vp, vp, vp]
         L.ep_dispatch_backward.restype = st
@@ -113,6 +117,8 @@ def lib() -> ctypes.CDLL:
         L.ep_combine_backward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp]
         L.ep_check_cvt_e4m3.restype = st
         L.ep_check_cvt_e4m3.argtypes = [vp, vp, ctypes.c_int64, vp]
+        L.ep_check_cvt_e2m1.restype = st
+        L.ep_check_cvt_e2m1.argtypes = [vp, vp, ctypes.c_int64, vp]
         L.ep_check_cvt_bf16.restype = st
         L.ep_check_cvt_bf16.argtypes = [vp, vp, ctypes.c_int64, vp]
         _lib = L
@@ -199,20 +205,52 @@ def ep_layout(shape: EpShape, topk_idx, expert_count, expert_offset, rank_count,
     _check("ep_layout", lib().ep_layout(ctypes.byref(shape.c()), *args, nbytes, _stream(stream)))
 
 
-def ep_dispatch(shape: EpShape, x, slot, recv_dtype: int, recv_x, recv_scale=None, stream=None) -> None:
-    T, H, k = shape.num_tokens, shape.hidden, shape.num_topk
-    rows = ep_recv_rows(shape)
+def recv_layout(shape: EpShape, recv_dtype: int):
+    """(bytes per receive row, scale entries per row, scale dtype) of a dispatch format."""
+    H = shape.hidden
     if recv_dtype == EP_BF16:
-        rx = _ptr(recv_x, "recv_x", _BF16_LIKE, rows * H)
-        rs = None
-    elif recv_dtype == EP_FP8_E4M3:
-        rx = _ptr(recv_x, "recv_x", _BYTE_LIKE, rows * H)
-        rs = _ptr(recv_scale, "recv_scale", torch.float32, rows * (H // 128))
+        return 2 * H, 0, None
+    if recv_dtype == EP_FP8_E4M3:
+        return H, H // 128, torch.float32
+    if recv_dtype == EP_MXFP8_E4M3:
+        return H, H // 32, torch.uint8
+    if recv_dtype == EP_MXFP4_E2M1:
+        return H // 2, H // 32, torch.uint8
+    raise ValueError(f"unknown recv_dtype {recv_dtype}")
+
+
+def _dispatch_args(shape: EpShape, x, slot, recv_dtype: int, recv_x, recv_scale):
+    T, H, k = shape.num_tokens, shape.hidden, shape.num_topk
+    rows = shape.recv_rows
+    row_bytes, nsc, sdt = recv_layout(shape, recv_dtype)
+    if recv_dtype == EP_BF16:
+        rx, rs = _ptr(recv_x, "recv_x", _BF16_LIKE, rows * H), None
     else:
-        raise ValueError(f"unknown recv_dtype {recv_dtype}")
-    _check("ep_dispatch", lib().ep_dispatch(
-        ctypes.byref(shape.c()), _ptr(x, "x", _BF16_LIKE, T * H, optional=T == 0),
-        _ptr(slot, "slot", torch.int32, T * k, optional=T == 0), int(recv_dtype), rx, rs, _stream(stream)))
+        rx = _ptr(recv_x, "recv_x", _BYTE_LIKE, rows * row_bytes)
+        rs = _ptr(recv_scale, "recv_scale", sdt if sdt is torch.float32 else _BYTE_LIKE, rows * nsc)
+    return (shape.c_ref, _ptr(x, "x", _BF16_LIKE, T * H, optional=T == 0),
+            _ptr(slot, "slot", torch.int32, T * k, optional=T == 0), int(recv_dtype), rx, rs)
+
+
+def _prequantized_args(shape: EpShape, x_q, x_scale, slot, recv_x, recv_scale):
+    T, H, k = shape.num_tokens, shape.hidden, shape.num_topk
+    rows = shape.recv_rows
+    return (shape.c_ref, _ptr(x_q, "x_q", _BYTE_LIKE, T * H, optional=T == 0),
+            _ptr(x_scale, "x_scale", torch.float32, T * (H // 128), optional=T == 0),
+            _ptr(slot, "slot", torch.int32, T * k, optional=T == 0),
+            _ptr(recv_x, "recv_x", _BYTE_LIKE, rows * H, optional=T == 0),
+            _ptr(recv_scale, "recv_scale", torch.float32, rows * (H // 128), optional=T == 0))
+
+
+def ep_dispatch(shape: EpShape, x, slot, recv_dtype: int, recv_x, recv_scale=None, stream=None) -> None:
+    _check("ep_dispatch", lib().ep_dispatch(*_dispatch_args(shape, x, slot, recv_dtype, recv_x, recv_scale),
+                                            _stream(stream)))
+
+
+def ep_dispatch_prequantized(shape: EpShape, x_q, x_scale, slot, recv_x, recv_scale, stream=None) -> None:
+    """Scatter caller-quantised E4M3 codes [T, H] and fp32 block scales [T, H/128] to every valid slot."""
+    _check("ep_dispatch_prequantized", lib().ep_dispatch_prequantized(
+        *_prequantized_args(shape, x_q, x_scale, slot, recv_x, recv_scale), _stream(stream)))
 
 
 def ep_combine(shape: EpShape, y, slot, topk_weights, out, stream=None) -> None:
@@ -261,6 +299,13 @@ def ep_combine_backward(shape: EpShape, grad_out, y, slot, topk_weights, grad_y,
 def ep_check_cvt_e4m3(inp, out, stream=None) -> None:
     n = inp.numel()
     _check("ep_check_cvt_e4m3", lib().ep_check_cvt_e4m3(
+        _ptr(inp, "in", torch.float32, n, optional=n == 0), _ptr(out, "out", _BYTE_LIKE, n, optional=n == 0),
+        n, _stream(stream)))
+
+
+def ep_check_cvt_e2m1(inp, out, stream=None) -> None:
+    n = inp.numel()
+    _check("ep_check_cvt_e2m1", lib().ep_check_cvt_e2m1(
         _ptr(inp, "in", torch.float32, n, optional=n == 0), _ptr(out, "out", _BYTE_LIKE, n, optional=n == 0),
         n, _stream(stream)))
 
@@ -319,18 +364,14 @@ def prepare_layout(shape: EpShape, topk_idx, expert_count, expert_offset, rank_c
 
 
 def prepare_dispatch(shape: EpShape, x, slot, recv_dtype: int, recv_x, recv_scale=None, stream=None) -> Prepared:
-    T, H, k = shape.num_tokens, shape.hidden, shape.num_topk
-    rows = shape.recv_rows
-    if recv_dtype == EP_BF16:
-        rx, rs = _ptr(recv_x, "recv_x", _BF16_LIKE, rows * H), None
-    elif recv_dtype == EP_FP8_E4M3:
-        rx = _ptr(recv_x, "recv_x", _BYTE_LIKE, rows * H)
-        rs = _ptr(recv_scale, "recv_scale", torch.float32, rows * (H // 128))
-    else:
-        raise ValueError(f"unknown recv_dtype {recv_dtype}")
-    args = (shape.c_ref, _ptr(x, "x", _BF16_LIKE, T * H, optional=T == 0),
-            _ptr(slot, "slot", torch.int32, T * k, optional=T == 0), int(recv_dtype), rx, rs)
-    return Prepared("ep_dispatch", lib().ep_dispatch, args, (x, slot, recv_x, recv_scale), stream)
+    return Prepared("ep_dispatch", lib().ep_dispatch, _dispatch_args(shape, x, slot, recv_dtype, recv_x, recv_scale),
+                    (x, slot, recv_x, recv_scale), stream)
+
+
+def prepare_dispatch_prequantized(shape: EpShape, x_q, x_scale, slot, recv_x, recv_scale, stream=None) -> Prepared:
+    return Prepared("ep_dispatch_prequantized", lib().ep_dispatch_prequantized,
+                    _prequantized_args(shape, x_q, x_scale, slot, recv_x, recv_scale),
+                    (x_q, x_scale, slot, recv_x, recv_scale), stream)
 
 
 def prepare_combine(shape: EpShape, y, slot, topk_weights, out, stream=None) -> Prepared:
@@ -394,8 +435,10 @@ class LayoutBuffers:
 
 
 def alloc_recv(shape: EpShape, recv_dtype: int, device="cuda"):
+    """Receive buffers of a dispatch format: (recv_x, recv_scale or None)."""
     rows, H = ep_recv_rows(shape), shape.hidden
     if recv_dtype == EP_BF16:
         return torch.empty((rows, H), dtype=torch.bfloat16, device=device), None
-    return (torch.empty((rows, H), dtype=torch.uint8, device=device),
-            torch.empty((rows, H // 128), dtype=torch.float32, device=device))
+    row_bytes, nsc, sdt = recv_layout(shape, recv_dtype)
+    return (torch.empty((rows, row_bytes), dtype=torch.uint8, device=device),
+            torch.empty((rows, nsc), dtype=sdt, device=device))

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 3
+#define EP_ABI_VERSION 4
 
 /* Limits checked by every entry point (EP_ERR_UNSUPPORTED beyond them). */
 #define EP_MAX_EXPERTS 2048
@@ -104,8 +104,10 @@ typedef struct ep_shape_t {
 } ep_shape_t;
 
 typedef enum ep_dtype_t {
-    EP_BF16 = 0,      /* receive rows are BF16 copies of the tokens        */
-    EP_FP8_E4M3 = 1   /* receive rows are OCP E4M3FN codes + fp32 scales    */
+    EP_BF16 = 0,        /* receive rows are BF16 copies of the tokens            */
+    EP_FP8_E4M3 = 1,    /* OCP E4M3FN codes + one fp32 scale per 128 columns     */
+    EP_MXFP8_E4M3 = 2,  /* OCP MX: E4M3 codes + one E8M0 scale per 32 columns    */
+    EP_MXFP4_E2M1 = 3   /* OCP MX: E2M1 codes, 2 per byte, + E8M0 per 32 columns */
 } ep_dtype_t;
 
 typedef enum ep_status_t {
@@ -178,13 +180,48 @@ ep_status_t ep_layout(const ep_shape_t *shape, const int32_t *topk_idx,
  *                           block b, s = max(amax_b, 1e-4) / 448 and
  *                           code = E4M3_RNE_SAT(x / s), both in fp32, with
  *                           a correctly rounded division
- *   recv_x     [ep_recv_rows, H], 16-byte aligned; rows that no pair maps
- *              to are left untouched
- *   recv_scale fp32 [ep_recv_rows, H/128] for FP8, else ignored (may be NULL)
+ *              EP_MXFP8_E4M3, EP_MXFP4_E2M1: the OCP Microscaling (MX v1.0)
+ *                           formats MI355X's matrix cores read, the
+ *                           counterpart of the 4-bit dispatch of DeepEP's
+ *                           Hybrid-EP branch ([GN] "Ramas experimentales y
+ *                           forks de la comunidad").  Per 32-column block b:
+ *                           e = floor(log2 amax_b) - emax (8 for E4M3, 2 for
+ *                           E2M1), clamped to [-127, 127], -127 for an
+ *                           all-zero block; element = RNE(x * 2^-e)
+ *                           saturated to the largest normal (448 / 6), sign
+ *                           kept; recv_scale[row, b] = e + 127 (E8M0 byte).
+ *                           MXFP8 rows are [H] bytes, MXFP4 rows [H/2] bytes
+ *                           with column 2i in the low nibble of byte i.
+ *                           H must be a multiple of 32.
+ *   recv_x     [ep_recv_rows, H] (BF16, E4M3, MXFP8) or [ep_recv_rows, H/2]
+ *              bytes (MXFP4), 16-byte aligned; rows that no pair maps to
+ *              are left untouched
+ *   recv_scale fp32 [ep_recv_rows, H/128] for EP_FP8_E4M3, uint8
+ *              [ep_recv_rows, H/32] for the MX formats; ignored (may be
+ *              NULL) for EP_BF16
  */
 ep_status_t ep_dispatch(const ep_shape_t *shape, const void *x, const int32_t *slot,
-                        ep_dtype_t recv_dtype, void *recv_x, float *recv_scale,
+                        ep_dtype_t recv_dtype, void *recv_x, void *recv_scale,
                         hipStream_t stream);
+
+/*
+ * Dispatch of tokens the caller has already quantised: DeepEP's dispatch
+ * takes FP8 input as a (data, scale factors) pair ([DOC] item 10).  Every
+ * valid pair (t, j) receives the codes and scales of token t unchanged (a
+ * byte scatter): recv_x[slot[t, j], :] = x_q[t, :] and
+ * recv_scale[slot[t, j], :] = x_scale[t, :].  Feeding it the output of an
+ * EP_FP8_E4M3 ep_dispatch to rows 0..T-1 reproduces ep_dispatch's result.
+ *
+ *   x_q         uint8 [T, H]          E4M3 codes (any bytes), 16-byte aligned
+ *   x_scale     fp32 [T, H/128]       block scales
+ *   slot        int32 [T, k]          from ep_layout
+ *   recv_x      uint8 [ep_recv_rows, H], 16-byte aligned; unmapped rows untouched
+ *   recv_scale  fp32 [ep_recv_rows, H/128]
+ * H must be a multiple of 128.
+ */
+ep_status_t ep_dispatch_prequantized(const ep_shape_t *shape, const void *x_q,
+                                     const float *x_scale, const int32_t *slot,
+                                     void *recv_x, float *recv_scale, hipStream_t stream);
 
 /*
  * Combine: the expert outputs are reduced back to token order
@@ -264,11 +301,14 @@ int ep_last_hip_error(void);
  *                      its rounding half-step), which covers every quotient
  *                      FP8 dispatch produces (|x / s| <= 448 plus one ulp)
  *   ep_check_cvt_bf16: out[i] = BF16_RNE(in[i]) for finite in[i]
+ *   ep_check_cvt_e2m1: out[i] = E2M1 code (low 4 bits) of in[i], nearest
+ *                      with ties to even, saturating at +-6, sign kept
  * in is a device fp32 array of n elements, out a device array of n codes
  * (uint8) or BF16 bit patterns (uint16); n >= 0.
  */
 ep_status_t ep_check_cvt_e4m3(const float *in, uint8_t *out, int64_t n, hipStream_t stream);
 ep_status_t ep_check_cvt_bf16(const float *in, uint16_t *out, int64_t n, hipStream_t stream);
+ep_status_t ep_check_cvt_e2m1(const float *in, uint8_t *out, int64_t n, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -67,6 +67,7 @@ def lib():
         L.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
         L.oracle_e2m1_encode.restype = ctypes.c_uint8
         L.oracle_e2m1_encode.argtypes = [ctypes.c_float]
+        L.oracle_e2m1_encode_array.argtypes = [vp, vp, i64]
         L.oracle_mx_exponent.restype = ctypes.c_int
         L.oracle_mx_exponent.argtypes = [ctypes.c_float, ctypes.c_int]
         L.oracle_dispatch_mx.argtypes = [i64, i64, i64, ctypes.c_int, vp, vp, vp, vp]
@@ -211,9 +212,10 @@ def dispatch_prequantized(x_q: np.ndarray, x_s: np.ndarray, slot: np.ndarray, ro
 
 
 def e2m1_encode(f) -> np.ndarray:
-    L = lib()
-    a = np.asarray(f, dtype=np.float32)
-    return np.array([L.oracle_e2m1_encode(float(v)) for v in a.ravel()], np.uint8).reshape(a.shape)
+    f = _c(np.asarray(f, dtype=np.float32), np.float32)
+    out = np.empty(f.shape, np.uint8)
+    lib().oracle_e2m1_encode_array(_p(f), _p(out), f.size)
+    return out
 
 
 def e2m1_decode(codes) -> np.ndarray:

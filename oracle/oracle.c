@@ -505,6 +505,12 @@ uint8_t oracle_e2m1_encode(float v)
     return (uint8_t)(sign | code);
 }
 
+void oracle_e2m1_encode_array(const float *in, uint8_t *out, int64_t n)
+{
+    int64_t i;
+    for (i = 0; i < n; ++i) out[i] = oracle_e2m1_encode(in[i]);
+}
+
 /*
  * MX block scale exponent (R14): e = floor(log2(amax)) - emax, clamped to
  * [-127, 127]; amax == 0 gives -127.  emax is the element format's largest

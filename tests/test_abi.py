@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_abi_version_and_status_strings(L):
     header = open(HEADER).read()
-    assert ep.ep_abi_version() == int(re.search(r"#define EP_ABI_VERSION (\d+)", header).group(1)) == 3
+    assert ep.ep_abi_version() == int(re.search(r"#define EP_ABI_VERSION (\d+)", header).group(1)) == 4
     for code in range(6):
         s = ep.ep_status_string(code)
         assert s.startswith("EP_"), s
@@ -119,6 +119,7 @@ def test_bad_shapes_rejected(L, kw, code):
     assert L.ep_layout_workspace_bytes(ctypes.byref(shape_c(**kw)), ctypes.byref(ws)) == code
     assert L.ep_layout(ctypes.byref(shape_c(**kw)), *([None] * 9), 0, None) == code
     assert L.ep_dispatch(ctypes.byref(shape_c(**kw)), None, None, 0, None, None, None) == code
+    assert L.ep_dispatch_prequantized(ctypes.byref(shape_c(**kw)), *([None] * 5), None) == code
     assert L.ep_combine(ctypes.byref(shape_c(**kw)), None, None, None, None, None) == code
     assert L.ep_dispatch_backward(ctypes.byref(shape_c(**kw)), None, None, None, None) == code
     assert L.ep_combine_backward(ctypes.byref(shape_c(**kw)), *([None] * 6), None) == code
@@ -171,6 +172,31 @@ def test_dispatch_argument_checks(L):
     assert L.ep_dispatch(ctypes.byref(shape_c(num_tokens=0)), None, None, 1, None, None, None) == OK
 
 
+def test_mx_dispatch_argument_checks(L):
+    s = ctypes.byref(shape_c())
+    for dt in (2, 3):
+        assert L.ep_dispatch(s, FAKE, FAKE, dt, FAKE, None, None) == INVALID          # MX needs scales
+        assert L.ep_dispatch(s, FAKE, FAKE, dt, FAKE, FAKE + 2, None) == MISALIGNED    # scales 4-byte
+        assert L.ep_dispatch(ctypes.byref(shape_c(hidden=48)), FAKE, FAKE, dt, FAKE, FAKE, None) == UNSUPPORTED
+        assert L.ep_dispatch(ctypes.byref(shape_c(num_tokens=0)), None, None, dt, None, None, None) == OK
+    assert L.ep_dispatch(s, FAKE, FAKE, 4, FAKE, FAKE, None) == INVALID               # no dtype 4
+    assert L.ep_dispatch(ctypes.byref(shape_c(hidden=160)), FAKE, FAKE, 1, FAKE, FAKE, None) == UNSUPPORTED
+
+
+def test_prequantized_dispatch_argument_checks(L):
+    s = ctypes.byref(shape_c())
+    for i in range(5):
+        q = [FAKE] * 5
+        q[i] = None
+        assert L.ep_dispatch_prequantized(s, *q, None) == INVALID, i
+    for i, off in ((0, 8), (1, 2), (2, 2), (3, 8), (4, 2)):
+        q = [FAKE] * 5
+        q[i] += off
+        assert L.ep_dispatch_prequantized(s, *q, None) == MISALIGNED, i
+    assert L.ep_dispatch_prequantized(ctypes.byref(shape_c(hidden=160)), *([FAKE] * 5), None) == UNSUPPORTED
+    assert L.ep_dispatch_prequantized(ctypes.byref(shape_c(num_tokens=0)), *([None] * 5), None) == OK
+
+
 def test_combine_argument_checks(L):
     s = ctypes.byref(shape_c())
     for i in range(4):
@@ -220,6 +246,9 @@ def test_check_helpers_argument_checks(L):
     assert L.ep_check_cvt_e4m3(FAKE + 1, FAKE, 4, None) == MISALIGNED
     assert L.ep_check_cvt_bf16(FAKE, FAKE + 1, 4, None) == MISALIGNED
     assert L.ep_check_cvt_e4m3(None, None, 0, None) == OK
+    assert L.ep_check_cvt_e2m1(None, None, -1, None) == INVALID
+    assert L.ep_check_cvt_e2m1(FAKE + 1, FAKE, 4, None) == MISALIGNED
+    assert L.ep_check_cvt_e2m1(None, None, 0, None) == OK
 
 
 def test_binding_rejects_host_tensors():

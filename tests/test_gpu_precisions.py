@@ -1,0 +1,199 @@
+"""GPU parity of the other dispatch precisions, through the C ABI, against the CPU oracle:
+MXFP8 / MXFP4 (E8M0 block scales) and the pre-quantised FP8 passthrough.  Codes, packed
+nibbles and scales must match bit for bit; rows no pair maps to stay untouched."""
+import dataclasses
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import combine_ep_layout_02_amd as ep
+from combine_ep_layout_02_amd import workloads as wl
+from test_gpu_parity import DEV, _idx, dev_bf16, dev_f32, dev_i32, inputs, log, setup_module, shape_of  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+
+MX = {8: ep.EP_MXFP8_E4M3, 4: ep.EP_MXFP4_E2M1}
+
+
+def run_mx(shape, x_bits, slot, elem_bits):
+    dt = MX[elem_bits]
+    row_bytes, nsc, _ = ep.recv_layout(shape, dt)
+    rows = shape.recv_rows
+    rq = torch.full((rows, row_bytes), 0x5A, dtype=torch.uint8, device=DEV)
+    rs = torch.full((rows, nsc), 0xEE, dtype=torch.uint8, device=DEV)
+    ep.ep_dispatch(shape, dev_bf16(x_bits), dev_i32(slot), dt, rq, rs)
+    torch.cuda.synchronize()
+    return rq.cpu().numpy(), rs.cpu().numpy()
+
+
+def check_mx(w, x_bits, lay, elem_bits, shape=None, tokens=None):
+    shape = shape or shape_of(w)
+    q, s = run_mx(shape, x_bits, lay.slot, elem_bits)
+    held = lay.src_pair >= 0
+    assert (q[~held] == 0x5A).all() and (s[~held] == 0xEE).all()
+    if tokens is None:
+        wq, ws = oracle.dispatch_mx(x_bits, lay.slot, w.recv_rows, elem_bits)
+        assert np.array_equal(q[held], wq[held]) and np.array_equal(s[held], ws[held])
+    else:
+        wq, ws = oracle.dispatch_mx(x_bits[tokens], lay.slot[tokens], w.recv_rows, elem_bits)
+        rows = lay.slot[tokens].ravel()
+        rows = rows[rows >= 0]
+        assert np.array_equal(q[rows], wq[rows]) and np.array_equal(s[rows], ws[rows])
+
+
+@pytest.mark.parametrize("elem_bits", [8, 4])
+@pytest.mark.parametrize("name", ["tiny", "mid", "decode", "v3"])
+def test_mx_dispatch_matches_oracle(name, elem_bits):
+    w, inp, lay = inputs(name)
+    log(f"[mx{elem_bits}] {name}")
+    check_mx(w, inp.x, lay, elem_bits)
+
+
+def special_blocks(rng, T, H):
+    """Rows whose 32-column blocks hit the format's corners: all zero, all subnormal BF16,
+    huge (near the BF16 maximum), a single non-zero element, exact ties after scaling,
+    saturation (amax just below the next power of two), negative zeros."""
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    nb = H // 32
+    for t in range(T):
+        for b in range(nb):
+            kind = (t * nb + b) % 8
+            blk = x[t, 32 * b:32 * b + 32]
+            if kind == 0:
+                blk[:] = 0.0
+            elif kind == 1:
+                blk[:] = rng.integers(-127, 128, 32).astype(np.float32) * np.float32(2.0 ** -133)
+            elif kind == 2:
+                blk[:] *= np.float32(2.0 ** 120)
+            elif kind == 3:
+                blk[:] = 0.0
+                blk[rng.integers(32)] = np.float32(rng.standard_normal() * 1e-3)
+            elif kind == 4:  # values on the E2M1 / E4M3 midpoints after scaling by 2^-e with amax 4 -> e = -6 / 0
+                blk[:] = rng.choice(np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 4.0, -0.25, -1.25, -3.5],
+                                             np.float32), 32)
+                blk[0] = 4.0
+            elif kind == 5:
+                blk[:] *= np.float32(0.01)
+                blk[3] = np.float32(1.9921875 * 2.0 ** 5)   # the top BF16 below 64: saturates after scaling
+            elif kind == 6:
+                blk[:] = -0.0
+                blk[5] = 1.0
+    return wl.f32_to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("elem_bits", [8, 4])
+@pytest.mark.parametrize("case", [
+    # name, T, H, k, E, C, mask, num_cus
+    ("h32_one_block", 64, 32, 2, 8, 0, 0.0, 0),
+    ("h160_partial_chunk", 100, 160, 3, 16, 0, 0.1, 0),
+    ("h1024_specials", 96, 1024, 4, 16, 0, 0.0, 0),
+    ("h9216_two_slices", 40, 9216, 4, 32, 0, 0.0, 0),
+    ("h16384", 12, 16384, 2, 8, 0, 0.0, 0),
+    ("padded_drops", 200, 512, 4, 16, 30, 0.0, 0),
+    ("budget_3", 300, 1024, 4, 16, 0, 0.05, 3),
+], ids=lambda c: c[0] if isinstance(c, tuple) else str(c))
+def test_mx_dispatch_edge_cases(case, elem_bits):
+    name, T, H, k, E, C, mask, n = case
+    log(f"[mx{elem_bits}-edge] {name}")
+    w = wl.custom(name, T, H, E, 4, k, seed=96, capacity=C)
+    rng = np.random.default_rng(96)
+    lay = oracle.layout(_idx(rng, T, k, E, mask), E, 4, 1, C)
+    x = special_blocks(rng, T, H)
+    check_mx(w, x, lay, elem_bits, shape=dataclasses.replace(shape_of(w), num_cus=n))
+
+
+def test_e2m1_conversion_exhaustive():
+    """Every float32 with |v| <= 8, both signs, plus the far range: the device E2M1 rounding
+    equals the oracle encoder."""
+    top = int(np.array([8.0], np.float32).view(np.uint32)[0])
+    chunk = 1 << 27
+    log(f"[cvt-e2m1] {2 * (top + 1)} values")
+    pool = ThreadPoolExecutor(16)
+    bad = 0
+    out = torch.empty(chunk, dtype=torch.uint8, device=DEV)
+    for lo in range(0, top + 1, chunk):
+        n = min(chunk, top + 1 - lo)
+        for sign in (0, 0x80000000):
+            bits = torch.arange(lo, lo + n, dtype=torch.int64, device=DEV) | sign
+            v = bits.to(torch.int32).view(torch.float32) if sign == 0 else \
+                (bits - (1 << 32)).to(torch.int32).view(torch.float32)
+            ep.ep_check_cvt_e2m1(v, out[:n])
+            got = out[:n].cpu().numpy()
+            vh = v.cpu().numpy()
+            parts = np.array_split(np.arange(n), 16)
+            want = np.concatenate(list(pool.map(lambda ix: oracle.e2m1_encode(vh[ix]), parts)))
+            bad += int((got != want).sum())
+    pool.shutdown()
+    big = torch.tensor([8.5, 100.0, 3e38, -9.0, -1e30], device=DEV)
+    outb = torch.empty(5, dtype=torch.uint8, device=DEV)
+    ep.ep_check_cvt_e2m1(big, outb)
+    assert bad == 0
+    assert outb.cpu().tolist() == oracle.e2m1_encode(big.cpu().numpy()).tolist() == [7, 7, 7, 15, 15]
+
+
+# --------------------------------------------------------------------------
+# pre-quantised FP8 passthrough
+# --------------------------------------------------------------------------
+
+def run_prequantized(shape, xq, xs, slot):
+    rows = shape.recv_rows
+    rq = torch.full((rows, shape.hidden), 0x5A, dtype=torch.uint8, device=DEV)
+    rs = torch.full((rows, shape.hidden // 128), -1.0, dtype=torch.float32, device=DEV)
+    ep.ep_dispatch_prequantized(shape, torch.from_numpy(xq).to(DEV), dev_f32(xs), dev_i32(slot), rq, rs)
+    torch.cuda.synchronize()
+    return rq.cpu().numpy(), rs.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "v3"])
+def test_prequantized_matches_oracle(name):
+    w, inp, lay = inputs(name)
+    log(f"[prequant] {name}")
+    rng = np.random.default_rng(w.seed)
+    xq = rng.integers(0, 256, (w.num_tokens, w.hidden), dtype=np.uint8)
+    xs = rng.standard_normal((w.num_tokens, w.hidden // 128)).astype(np.float32)
+    q, s = run_prequantized(shape_of(w), xq, xs, lay.slot)
+    wq, ws = oracle.dispatch_prequantized(xq, xs, lay.slot, w.recv_rows)
+    held = lay.src_pair >= 0
+    assert np.array_equal(q[held], wq[held]) and np.array_equal(s[held], ws[held])
+    assert (q[~held] == 0x5A).all() and (s[~held] == -1.0).all()
+
+
+@pytest.mark.parametrize("case", [("h128", 50, 128, 2, 8, 0.0, 0), ("h16384_two_scale_regs", 20, 16384, 4, 16, 0.1, 0),
+                                  ("h8320_odd", 30, 8320, 3, 16, 0.0, 0), ("budget_2", 200, 1024, 4, 16, 0.1, 2)],
+                         ids=lambda c: c[0])
+def test_prequantized_edge_cases(case):
+    name, T, H, k, E, mask, n = case
+    log(f"[prequant-edge] {name}")
+    w = wl.custom(name, T, H, E, 4, k, seed=97)
+    rng = np.random.default_rng(97)
+    lay = oracle.layout(_idx(rng, T, k, E, mask), E, 4)
+    xq = rng.integers(0, 256, (T, H), dtype=np.uint8)
+    xs = rng.standard_normal((T, H // 128)).astype(np.float32)
+    q, s = run_prequantized(dataclasses.replace(shape_of(w), num_cus=n), xq, xs, lay.slot)
+    wq, ws = oracle.dispatch_prequantized(xq, xs, lay.slot, w.recv_rows)
+    held = lay.src_pair >= 0
+    assert np.array_equal(q[held], wq[held]) and np.array_equal(s[held], ws[held])
+    assert (q[~held] == 0x5A).all()
+
+
+def test_quantise_then_passthrough_equals_fp8_dispatch():
+    """An FP8 dispatch of the 8192-token batch to rows 0..T-1, passed through with the
+    real slots, gives the fused FP8 dispatch's bytes."""
+    w, inp, lay = inputs("v3")
+    shape = shape_of(w)
+    T = w.num_tokens
+    ident = ep.EpShape(T, w.hidden, 1, w.num_experts, w.num_ranks)
+    xq = torch.empty((T, w.hidden), dtype=torch.uint8, device=DEV)
+    xs = torch.empty((T, w.hidden // 128), dtype=torch.float32, device=DEV)
+    x = dev_bf16(inp.x)
+    ep.ep_dispatch(ident, x, torch.arange(T, dtype=torch.int32, device=DEV)[:, None], ep.EP_FP8_E4M3, xq, xs)
+    rq1, rs1 = ep.alloc_recv(shape, ep.EP_FP8_E4M3, DEV)
+    rq2, rs2 = ep.alloc_recv(shape, ep.EP_FP8_E4M3, DEV)
+    slot = dev_i32(lay.slot)
+    ep.ep_dispatch_prequantized(shape, xq, xs, slot, rq1, rs1)
+    ep.ep_dispatch(shape, x, slot, ep.EP_FP8_E4M3, rq2, rs2)
+    torch.cuda.synchronize()
+    assert torch.equal(rq1, rq2) and torch.equal(rs1, rs2)

@@ -328,7 +328,16 @@ __global__ __launch_bounds__(64 * WPB) void dispatch_mx_kernel(RowParams p, int 
     }
     if (lane < 4 * sl.nc) {
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(sdst + (int64_t)s * nb, (uint32_t)nb);
-      __builtin_amdgcn_raw_buffer_store_b32(my_sdw, rs, (int)scol, 0, AUX_ST);
+      if (scol + 4u <= (uint32_t)nb) {
+        __builtin_amdgcn_raw_buffer_store_b32(my_sdw, rs, (int)scol, 0, AUX_ST);
+      } else {
+        // the row's last scales when H / 32 is not a multiple of 4: a dword
+        // reaching past the row would be dropped whole by the range check,
+        // so store byte by byte (bytes past the row are dropped)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(my_sdw >> (8 * b)), rs, (int)scol + b, 0, AUX_ST);
+      }
     }
   }
   }

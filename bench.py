@@ -222,25 +222,24 @@ def time_backward(step, reps):
     dbw = ep.prepare_dispatch_backward(step.shape, grad_recv, step.lay.slot, grad_x, stream)
     cbw = ep.prepare_combine_backward(step.shape, grad_out, step.y, step.lay.slot, step.wts, grad_y, grad_w,
                                       stream)
-    for _ in range(3):
-        dbw()
-        cbw()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
-    torch.cuda.synchronize()
-    for e in ev:
-        e[0].record()
-        dbw()
-        e[1].record()
-        cbw()
-        e[2].record()
-    torch.cuda.synchronize()
-    ms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(2)] for e in ev])
-    d_us, c_us = np.median(ms, axis=0) * 1e3
+    meds = []
+    for fn in (dbw, cbw):   # each in a loop of its own: steady state of that kernel alone
+        for _ in range(3):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        meds.append(float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3)
+    d_us, c_us = meds
     db, cb = bytes_dispatch_backward(w), bytes_combine_backward(w)
     return {"dispatch_backward": {"us": round(float(d_us), 2), "bytes": db, "GBps": round(db / d_us / 1e3, 1)},
             "combine_backward": {"us": round(float(c_us), 2), "bytes": cb, "GBps": round(cb / c_us / 1e3, 1)},
-            "note": f"medians of {reps} calls with events around each, on the step's routing handle; "
-                    "combine_backward includes the gate-weight gradient"}
+            "note": f"medians of {reps} back-to-back calls of each with events around each call, on the "
+                    "step's routing handle; combine_backward includes the gate-weight gradient"}
 
 
 def cu_sweep(dev, budgets, gemm_n=4096, reps=10):

@@ -133,10 +133,17 @@ class Step:
         self.dispatch = ep.prepare_dispatch(self.shape, self.x, self.lay.slot, self.dtype, self.recv_x,
                                             self.recv_scale, stream)
         self.combine = ep.prepare_combine(self.shape, self.y, self.lay.slot, self.wts, self.out, stream)
+        # layout and dispatch as one call (one launch when the batch is one layout tile)
+        self.layout_dispatch = self.lay.prepare_dispatch(self.idx, self.x, self.dtype, self.recv_x, self.recv_scale,
+                                                         stream)
 
     def run(self):
         self.layout()
         self.dispatch()
+        self.combine()
+
+    def run_fused(self):
+        self.layout_dispatch()
         self.combine()
 
     @property
@@ -144,17 +151,18 @@ class Step:
         return bytes_layout(self.w) + bytes_dispatch(self.w, self.fp8) + bytes_combine(self.w)
 
 
-def time_steps(step, steps, warmup):
+def time_steps(step, steps, warmup, fused=False):
     """Warm up, then time `steps` back-to-back steps between two HIP events on
     the launch stream (torch's current stream, which the binding launches on)."""
+    run = step.run_fused if fused else step.run
     for _ in range(warmup):
-        step.run()
+        run()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record()
     for _ in range(steps):
-        step.run()
+        run()
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end), time.perf_counter() - t0
@@ -546,16 +554,20 @@ def main():
         log("[bench] decode workload")
         dstep = Step(wl.WORKLOADS["decode"], dev, fp8=True)
         n = 500
-        d_total, _ = time_steps(dstep, n, 50)
+        d_total, _ = time_steps(dstep, n, 50, fused=True)
+        d_unfused, _ = time_steps(dstep, n, 50)
         d_stage = time_stages(dstep, 100)
         dec = {"us_per_call": round(d_total / n * 1e3, 2),
+               "us_per_call_separate_layout": round(d_unfused / n * 1e3, 2),
                "layout_us": round(float(np.median(d_stage[:, 0])) * 1e3, 2),
                "dispatch_us": round(float(np.median(d_stage[:, 1])) * 1e3, 2),
                "combine_us": round(float(np.median(d_stage[:, 2])) * 1e3, 2),
                "bytes": dstep.bytes,
-               "note": "one call = layout + FP8 dispatch + combine of 128 tokens into the padded [256, 128, 7168] "
-                       "layout; mean over 500 back-to-back calls (inputs stay in the 256 MB Infinity Cache); "
-                       "stage times are medians with events around each kernel"}
+               "note": "one call = layout + FP8 dispatch (ep_layout_dispatch: one launch for this one-tile batch) "
+                       "+ combine of 128 tokens into the padded [256, 128, 7168] layout; mean over 500 back-to-back "
+                       "calls (inputs stay in the 256 MB Infinity Cache); us_per_call_separate_layout runs "
+                       "ep_layout and ep_dispatch as two launches; stage times are medians with events around "
+                       "each kernel of the two-launch form"}
         del dstep
 
     configs = None

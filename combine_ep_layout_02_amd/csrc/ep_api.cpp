@@ -85,23 +85,24 @@ EP_EXPORT ep_status_t ep_layout_workspace_bytes(const ep_shape_t* shape, size_t*
   return EP_OK;
 }
 
-EP_EXPORT ep_status_t ep_layout(const ep_shape_t* shape, const int32_t* topk_idx, int32_t* expert_count,
-                                int32_t* expert_offset, int32_t* rank_count, int32_t* rank_offset, int32_t* slot,
-                                int32_t* src_pair, int32_t* diag, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
-  const ep_status_t st = check_shape(shape);
-  if (st != EP_OK) return st;
+namespace {
+
+// Checks of ep_layout's arguments (shape already checked) and its parameters.
+ep_status_t layout_args(const ep_shape_t* shape, const int32_t* topk_idx, int32_t* expert_count,
+                        int32_t* expert_offset, int32_t* rank_count, int32_t* rank_offset, int32_t* slot,
+                        int32_t* src_pair, int32_t* diag, void* workspace, size_t workspace_bytes,
+                        ep::LayoutPlan& pl, ep::LayoutParams& p) {
   const int T = shape->num_tokens;
   if (!expert_count || !expert_offset || !rank_count || !rank_offset) return EP_ERR_INVALID_ARG;
   if (T > 0 && (!topk_idx || !slot)) return EP_ERR_INVALID_ARG;
   const int32_t* ptrs[] = {topk_idx, expert_count, expert_offset, rank_count, rank_offset, slot, src_pair, diag};
   for (const int32_t* q : ptrs)
     if (!aligned(q, 4)) return EP_ERR_MISALIGNED;
-  const ep::LayoutPlan pl = ep::plan_layout(T, shape->num_topk, shape->num_experts, shape->num_ranks);
+  pl = ep::plan_layout(T, shape->num_topk, shape->num_experts, shape->num_ranks);
   if (!workspace || workspace_bytes < pl.ws_bytes) return EP_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return EP_ERR_MISALIGNED;
 
-  ep::LayoutParams p{};
+  p = ep::LayoutParams{};
   char* ws = static_cast<char*>(workspace);
   p.idx = topk_idx;
   p.expert_count = expert_count;
@@ -121,24 +122,23 @@ EP_EXPORT ep_status_t ep_layout(const ep_shape_t* shape, const int32_t* topk_idx
   p.A = shape->expert_alignment;
   p.C = shape->capacity;
   p.rows = recv_rows_of(shape);
-  return hip_status(ep::launch_layout(pl, p, stream));
+  return EP_OK;
 }
 
-EP_EXPORT ep_status_t ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t* slot,
-                                  ep_dtype_t recv_dtype, void* recv_x, void* recv_scale, hipStream_t stream) {
-  const ep_status_t st = check_shape(shape);
-  if (st != EP_OK) return st;
+// Checks of ep_dispatch's arguments (shape already checked) and its parameters.
+ep_status_t dispatch_args(const ep_shape_t* shape, const void* x, const int32_t* slot, ep_dtype_t recv_dtype,
+                          void* recv_x, void* recv_scale, ep::RowParams& p) {
   const bool mx = recv_dtype == EP_MXFP8_E4M3 || recv_dtype == EP_MXFP4_E2M1;
   if (recv_dtype != EP_BF16 && recv_dtype != EP_FP8_E4M3 && !mx) return EP_ERR_INVALID_ARG;
   if (recv_dtype == EP_FP8_E4M3 && shape->hidden % 128 != 0) return EP_ERR_UNSUPPORTED;
   if (mx && shape->hidden % 32 != 0) return EP_ERR_UNSUPPORTED;
   const int T = shape->num_tokens;
+  p = ep::RowParams{};
   if (T == 0) return EP_OK;
   if (!x || !slot || !recv_x) return EP_ERR_INVALID_ARG;
   if (recv_dtype != EP_BF16 && !recv_scale) return EP_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(slot, 4) || !aligned(recv_scale, 4))
     return EP_ERR_MISALIGNED;
-  ep::RowParams p{};
   p.src = x;
   p.slot = slot;
   p.dst = recv_x;
@@ -148,12 +148,66 @@ EP_EXPORT ep_status_t ep_dispatch(const ep_shape_t* shape, const void* x, const 
   p.k = shape->num_topk;
   p.rows = recv_rows_of(shape);
   p.num_cus = shape->num_cus;
+  return EP_OK;
+}
+
+hipError_t launch_dispatch(const ep::RowParams& p, ep_dtype_t recv_dtype, hipStream_t stream) {
+  if (p.T == 0) return hipSuccess;
   switch (recv_dtype) {
-    case EP_BF16: return hip_status(ep::launch_dispatch_bf16(p, stream));
-    case EP_FP8_E4M3: return hip_status(ep::launch_dispatch_fp8(p, stream));
-    case EP_MXFP8_E4M3: return hip_status(ep::launch_dispatch_mx(p, 8, stream));
-    default: return hip_status(ep::launch_dispatch_mx(p, 4, stream));
+    case EP_BF16: return ep::launch_dispatch_bf16(p, stream);
+    case EP_FP8_E4M3: return ep::launch_dispatch_fp8(p, stream);
+    case EP_MXFP8_E4M3: return ep::launch_dispatch_mx(p, 8, stream);
+    default: return ep::launch_dispatch_mx(p, 4, stream);
   }
+}
+
+}  // namespace
+
+EP_EXPORT ep_status_t ep_layout(const ep_shape_t* shape, const int32_t* topk_idx, int32_t* expert_count,
+                                int32_t* expert_offset, int32_t* rank_count, int32_t* rank_offset, int32_t* slot,
+                                int32_t* src_pair, int32_t* diag, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  const ep_status_t st = check_shape(shape);
+  if (st != EP_OK) return st;
+  ep::LayoutPlan pl;
+  ep::LayoutParams p;
+  const ep_status_t st2 = layout_args(shape, topk_idx, expert_count, expert_offset, rank_count, rank_offset, slot,
+                                      src_pair, diag, workspace, workspace_bytes, pl, p);
+  if (st2 != EP_OK) return st2;
+  return hip_status(ep::launch_layout(pl, p, stream));
+}
+
+EP_EXPORT ep_status_t ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t* slot,
+                                  ep_dtype_t recv_dtype, void* recv_x, void* recv_scale, hipStream_t stream) {
+  const ep_status_t st = check_shape(shape);
+  if (st != EP_OK) return st;
+  ep::RowParams p;
+  const ep_status_t st2 = dispatch_args(shape, x, slot, recv_dtype, recv_x, recv_scale, p);
+  if (st2 != EP_OK) return st2;
+  return hip_status(launch_dispatch(p, recv_dtype, stream));
+}
+
+EP_EXPORT ep_status_t ep_layout_dispatch(const ep_shape_t* shape, const int32_t* topk_idx, int32_t* expert_count,
+                                         int32_t* expert_offset, int32_t* rank_count, int32_t* rank_offset,
+                                         int32_t* slot, int32_t* src_pair, int32_t* diag, void* workspace,
+                                         size_t workspace_bytes, const void* x, ep_dtype_t recv_dtype, void* recv_x,
+                                         void* recv_scale, hipStream_t stream) {
+  const ep_status_t st = check_shape(shape);
+  if (st != EP_OK) return st;
+  ep::LayoutPlan pl;
+  ep::LayoutParams lp;
+  ep_status_t st2 = layout_args(shape, topk_idx, expert_count, expert_offset, rank_count, rank_offset, slot,
+                                src_pair, diag, workspace, workspace_bytes, pl, lp);
+  if (st2 != EP_OK) return st2;
+  ep::RowParams rp;
+  st2 = dispatch_args(shape, x, slot, recv_dtype, recv_x, recv_scale, rp);
+  if (st2 != EP_OK) return st2;
+  if (shape->num_tokens > 0 && shape->num_cus == 0 && (recv_dtype == EP_BF16 || recv_dtype == EP_FP8_E4M3) &&
+      ep::layout_dispatch_fusable(pl))
+    return hip_status(ep::launch_layout_dispatch(pl, lp, rp, recv_dtype == EP_FP8_E4M3, stream));
+  const hipError_t err = ep::launch_layout(pl, lp, stream);
+  if (err != hipSuccess) return hip_status(err);
+  return hip_status(launch_dispatch(rp, recv_dtype, stream));
 }
 
 EP_EXPORT ep_status_t ep_dispatch_prequantized(const ep_shape_t* shape, const void* x_q, const float* x_scale,

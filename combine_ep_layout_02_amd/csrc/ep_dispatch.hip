@@ -28,35 +28,16 @@
 // row return 0 and stores past it are dropped.
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
+#include "ep_dispatch_device.hpp"
 
 namespace ep {
 namespace {
 
+using namespace dsp;
+
 constexpr int kMaxChunks = 16;     // most 512-column chunks a wavefront holds (8192 columns)
 constexpr int kWavesPerBlock = 4;  // 256 threads (whole-GPU launches)
 constexpr int kMinWaves = 2048;    // 8 wavefronts per CU
-constexpr uint32_t kNoColumn = 0xFFFFFFF0u;  // a load offset past any row: reads 0
-
-// Loads the pair slots of token t into lanes 0..k-1 (one vector load), so a
-// wave-uniform slot is one v_readlane away.
-__device__ __forceinline__ int load_lane_slot(const int32_t* slot, int64_t t, int k, int lane) {
-  return lane < k ? slot[t * k + lane] : -1;
-}
-
-__device__ __forceinline__ bool slot_ok(int s, int64_t rows) { return s >= 0 && (int64_t)s < rows; }
-
-// Token and first chunk of slice `wave` (token-major: wpt slices per token).
-struct Slice {
-  int t, c0, nc;
-};
-
-__device__ __forceinline__ Slice slice_of(int wave, int wpt, int cpw, int nchunks) {
-  Slice sl;
-  sl.t = wave / wpt;
-  sl.c0 = (wave - sl.t * wpt) * cpw;
-  sl.nc = min(cpw, nchunks - sl.c0);
-  return sl;
-}
 
 // Slices are handed out grid-stride: a whole-GPU launch has one wavefront per
 // slice and runs the loop once; a launch limited to a CU budget runs that
@@ -66,143 +47,26 @@ __device__ __forceinline__ Slice slice_of(int wave, int wpt, int cpw, int nchunk
   for (int wave = uniform((int)blockIdx.x * (WPB) + (int)(threadIdx.x >> 6)); wave < (total); \
        wave += (int)gridDim.x * (WPB))
 
-template <int NC, int AUX_LD>
-__device__ __forceinline__ void load_row(const RowParams& p, const Slice& sl, int lane, u32x4 (&v)[NC]) {
-  const uint16_t* xrow = static_cast<const uint16_t*>(p.src) + (int64_t)sl.t * p.H;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(xrow, (uint32_t)p.H * 2u);
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-    v[c] = load16<AUX_LD>(rx, c < sl.nc ? (uint32_t)((sl.c0 + c) * 512 + lane * 8) * 2u : kNoColumn);
-}
-
-// Eight BF16 values times w, each product rounded to fp32 and then to BF16
-// (nearest even).
-__device__ __forceinline__ u32x4 scale8(u32x4 v, float w) {
-  u32x4 o;
-  o.x = pack_bf16x2(w * bf16_lo(v.x), w * bf16_hi(v.x));
-  o.y = pack_bf16x2(w * bf16_lo(v.y), w * bf16_hi(v.y));
-  o.z = pack_bf16x2(w * bf16_lo(v.z), w * bf16_hi(v.z));
-  o.w = pack_bf16x2(w * bf16_lo(v.w), w * bf16_hi(v.w));
-  return o;
-}
-
 // NC: chunk capacity of the instantiation (>= chunks per wavefront).
-// SCALED: copy j is BF16_RNE(w[t,j] * x[t]) instead of x[t] (the output-row
-// gradients of the combine backward: a dispatch scaled per copy).
 template <int NC, int AUX_LD, int AUX_ST, bool SCALED, int WPB>
 __global__ __launch_bounds__(64 * WPB) void dispatch_bf16_kernel(RowParams p, int wpt, int cpw, int nchunks) {
   const int lane = threadIdx.x & 63;
   EP_FOR_EACH_SLICE(WPB, p.T * wpt, wave) {
-  const Slice sl = slice_of(wave, wpt, cpw, nchunks);
-  u32x4 v[NC];
-  load_row<NC, AUX_LD>(p, sl, lane, v);
-  const int slots = load_lane_slot(p.slot, sl.t, p.k, lane);
-  int wl = 0;
-  if (SCALED && lane < p.k) wl = (int)__float_as_uint(p.weights[(int64_t)sl.t * p.k + lane]);
-
-  uint16_t* dst = static_cast<uint16_t*>(p.dst);
-  const uint32_t col = (uint32_t)(sl.c0 * 512 + lane * 8) * 2u;
-  for (int j = 0; j < p.k; ++j) {
-    const int s = __builtin_amdgcn_readlane(slots, j);
-    if (!slot_ok(s, p.rows)) continue;
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dst + (int64_t)s * p.H, (uint32_t)p.H * 2u);
-    if constexpr (SCALED) {
-      const float w = __uint_as_float((uint32_t)__builtin_amdgcn_readlane(wl, j));
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        // Re-widen the row for every copy: an empty asm makes the register
-        // opaque, so the compiler does not keep 8 * NC widened floats live
-        // across the j loop (which halves occupancy at NC = 14).
-        u32x4 vc = v[c];
-        asm volatile("" : "+v"(vc));
-        if (c < sl.nc) store16<AUX_ST>(rd, col + 1024u * c, scale8(vc, w));
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        if (c < sl.nc) store16<AUX_ST>(rd, col + 1024u * c, v[c]);
-    }
-  }
+    const Slice sl = slice_of(wave, wpt, cpw, nchunks);
+    u32x4 v[NC];
+    load_row<NC, AUX_LD>(p, sl, lane, v);
+    store_bf16_row<NC, AUX_ST, SCALED>(p, sl, lane, v, load_lane_slot(p.slot, sl.t, p.k, lane));
   }
 }
 
-// Eight BF16 values -> eight E4M3 codes with scale s: code = E4M3(x / s),
-// one correctly rounded fp32 division per element.
-__device__ __forceinline__ u32x2 quantize8(u32x4 v, float s) {
-  u32x2 q;
-  q.x = pack_e4m3x4(bf16_lo(v.x) / s, bf16_hi(v.x) / s, bf16_lo(v.y) / s, bf16_hi(v.y) / s);
-  q.y = pack_e4m3x4(bf16_lo(v.z) / s, bf16_hi(v.z) / s, bf16_lo(v.w) / s, bf16_hi(v.w) / s);
-  return q;
-}
-
-// Block scale: s = max(amax, 1e-4) / 448 (fp32, correctly rounded).  The
-// floor keeps an all-zero block finite; 448 is E4M3's largest magnitude, so
-// the block's largest element lands on the top code.
-__device__ __forceinline__ float block_scale(uint32_t amax_bits16) {
-  return fmaxf(__uint_as_float(amax_bits16 << 16), 1e-4f) / 448.0f;
-}
-
-// cpw (chunks per wavefront) is even, so chunks pair up as (2m, 2m+1): the
-// even lane of a lane pair stores 16 bytes of chunk 2m, the odd lane the same
-// bytes of chunk 2m+1.  A pair whose second chunk lies past the row stores
-// that half out of range, where the store is dropped.
 template <int NC, int AUX_LD, int AUX_ST, int WPB>
 __global__ __launch_bounds__(64 * WPB) void dispatch_fp8_kernel(RowParams p, int wpt, int cpw, int nchunks) {
-  static_assert(NC % 2 == 0, "chunks pair up");
   const int lane = threadIdx.x & 63;
   EP_FOR_EACH_SLICE(WPB, p.T * wpt, wave) {
-  const Slice sl = slice_of(wave, wpt, cpw, nchunks);
-  u32x4 v[NC];
-  load_row<NC, AUX_LD>(p, sl, lane, v);
-  const int slots = load_lane_slot(p.slot, sl.t, p.k, lane);
-
-  float sc[NC];
-  u32x2 q[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    sc[c] = block_scale(row16_max_u32(absmax_bits8(v[c])));
-    q[c] = quantize8(v[c], sc[c]);
-  }
-  const bool odd = lane & 1;
-  u32x4 out[NC / 2];
-#pragma unroll
-  for (int m = 0; m < NC / 2; ++m) {
-    const u32x2 a = q[2 * m], b = q[2 * m + 1];
-    const u32x2 send = odd ? a : b;
-    u32x2 recv;
-    recv.x = (uint32_t)__builtin_amdgcn_mov_dpp((int)send.x, 0xB1, 0xF, 0xF, false);
-    recv.y = (uint32_t)__builtin_amdgcn_mov_dpp((int)send.y, 0xB1, 0xF, 0xF, false);
-    out[m].x = odd ? recv.x : a.x;
-    out[m].y = odd ? recv.y : a.y;
-    out[m].z = odd ? b.x : recv.x;
-    out[m].w = odd ? b.y : recv.y;
-  }
-  // lane l < 4*nc takes the scale of block 4*c0 + l (chunk l/4, DPP row l%4)
-  float my_scale = 0.0f;
-  const int owner = (lane & 3) << 4;
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const float g = __shfl(sc[c], owner, 64);
-    if ((lane >> 2) == c) my_scale = g;
-  }
-
-  const int H = p.H, nb = H >> 7;
-  uint8_t* dst = static_cast<uint8_t*>(p.dst);
-  const uint32_t ocol = (uint32_t)(sl.c0 * 512) + (odd ? 512u : 0u) + 16u * (uint32_t)(lane >> 1);
-  const uint32_t scol = (uint32_t)(sl.c0 * 4 + lane) * 4u;
-  for (int j = 0; j < p.k; ++j) {
-    const int s = __builtin_amdgcn_readlane(slots, j);
-    if (!slot_ok(s, p.rows)) continue;
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dst + (int64_t)s * H, (uint32_t)H);
-#pragma unroll
-    for (int m = 0; m < NC / 2; ++m)
-      if (2 * m < sl.nc) store16<AUX_ST>(rd, ocol + 1024u * m, out[m]);
-    if (lane < 4 * sl.nc) {
-      const __amdgpu_buffer_rsrc_t rs =
-          make_rsrc(static_cast<float*>(p.recv_scale) + (int64_t)s * nb, (uint32_t)nb * 4u);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(my_scale), rs, (int)scol, 0, AUX_ST);
-    }
-  }
+    const Slice sl = slice_of(wave, wpt, cpw, nchunks);
+    u32x4 v[NC];
+    load_row<NC, AUX_LD>(p, sl, lane, v);
+    store_fp8_row<NC, AUX_ST>(p, sl, lane, v, load_lane_slot(p.slot, sl.t, p.k, lane));
   }
 }
 
@@ -423,14 +287,105 @@ __global__ __launch_bounds__(256) void check_cvt_bf16_kernel(const float* in, ui
   }
 }
 
-// Wavefronts per token, (even) chunks per wavefront and the launch shape.
-struct Split {
-  int nchunks, wpt, cpw, blocks;
-  bool budget;  // persistent kBudgetWaves-wavefront workgroups, one per CU of the budget
-};
 
-Split split_for(const RowParams& p) {
-  Split s;
+}  // namespace
+
+namespace {
+
+template <int NC, bool SCALED, int WPB>
+void launch_bf16_ncsw(const DispatchSplit& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  if (streaming)
+    hipLaunchKernelGGL((dispatch_bf16_kernel<NC, kAuxDefault, kAuxNT, SCALED, WPB>), dim3(s.blocks), dim3(64 * WPB),
+                       0, stream, p, s.wpt, s.cpw, s.nchunks);
+  else
+    hipLaunchKernelGGL((dispatch_bf16_kernel<NC, kAuxDefault, kAuxDefault, SCALED, WPB>), dim3(s.blocks),
+                       dim3(64 * WPB), 0, stream, p, s.wpt, s.cpw, s.nchunks);
+}
+
+template <int NC, bool SCALED>
+void launch_bf16_ncs(const DispatchSplit& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  if (s.budget)
+    launch_bf16_ncsw<NC, SCALED, kBudgetWaves>(s, p, streaming, stream);
+  else
+    launch_bf16_ncsw<NC, SCALED, kWavesPerBlock>(s, p, streaming, stream);
+}
+
+template <int NC>
+void launch_bf16_nc(const DispatchSplit& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  if (p.weights)
+    launch_bf16_ncs<NC, true>(s, p, streaming, stream);
+  else
+    launch_bf16_ncs<NC, false>(s, p, streaming, stream);
+}
+
+template <int NC, int WPB>
+void launch_fp8_ncw(const DispatchSplit& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  if (streaming)
+    hipLaunchKernelGGL((dispatch_fp8_kernel<NC, kAuxDefault, kAuxNT, WPB>), dim3(s.blocks), dim3(64 * WPB), 0, stream,
+                       p, s.wpt, s.cpw, s.nchunks);
+  else
+    hipLaunchKernelGGL((dispatch_fp8_kernel<NC, kAuxDefault, kAuxDefault, WPB>), dim3(s.blocks), dim3(64 * WPB), 0,
+                       stream, p, s.wpt, s.cpw, s.nchunks);
+}
+
+template <int NC, int WPB, int ELEM>
+void launch_mx_ncw(const DispatchSplit& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  if (streaming)
+    hipLaunchKernelGGL((dispatch_mx_kernel<NC, kAuxDefault, kAuxNT, WPB, ELEM>), dim3(s.blocks), dim3(64 * WPB), 0,
+                       stream, p, s.wpt, s.cpw, s.nchunks);
+  else
+    hipLaunchKernelGGL((dispatch_mx_kernel<NC, kAuxDefault, kAuxDefault, WPB, ELEM>), dim3(s.blocks),
+                       dim3(64 * WPB), 0, stream, p, s.wpt, s.cpw, s.nchunks);
+}
+
+template <int NC, int ELEM>
+void launch_mx_nce(const DispatchSplit& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  if (s.budget)
+    launch_mx_ncw<NC, kBudgetWaves, ELEM>(s, p, streaming, stream);
+  else
+    launch_mx_ncw<NC, kWavesPerBlock, ELEM>(s, p, streaming, stream);
+}
+
+template <int NC>
+void launch_mx8_nc(const DispatchSplit& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  launch_mx_nce<NC, 8>(s, p, streaming, stream);
+}
+
+template <int NC>
+void launch_mx4_nc(const DispatchSplit& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  launch_mx_nce<NC, 4>(s, p, streaming, stream);
+}
+
+template <int NC, int WPB>
+void launch_pq_ncw(const DispatchSplit& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  if (streaming)
+    hipLaunchKernelGGL((dispatch_prequantized_kernel<NC, kAuxDefault, kAuxNT, WPB>), dim3(s.blocks), dim3(64 * WPB),
+                       0, stream, p, s.wpt, s.cpw, s.nchunks);
+  else
+    hipLaunchKernelGGL((dispatch_prequantized_kernel<NC, kAuxDefault, kAuxDefault, WPB>), dim3(s.blocks),
+                       dim3(64 * WPB), 0, stream, p, s.wpt, s.cpw, s.nchunks);
+}
+
+template <int NC>
+void launch_pq_nc(const DispatchSplit& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  if (s.budget)
+    launch_pq_ncw<NC, kBudgetWaves>(s, p, streaming, stream);
+  else
+    launch_pq_ncw<NC, kWavesPerBlock>(s, p, streaming, stream);
+}
+
+template <int NC>
+void launch_fp8_nc(const DispatchSplit& s, const RowParams& p, bool streaming, hipStream_t stream) {
+  if (s.budget)
+    launch_fp8_ncw<NC, kBudgetWaves>(s, p, streaming, stream);
+  else
+    launch_fp8_ncw<NC, kWavesPerBlock>(s, p, streaming, stream);
+}
+
+}  // namespace
+
+DispatchSplit dispatch_split(const RowParams& p) {
+  DispatchSplit s;
   s.nchunks = (p.H + 511) / 512;
   s.budget = p.num_cus > 0;
   // Whole rows per wavefront for long bursts, unless the batch is too small
@@ -453,102 +408,6 @@ Split split_for(const RowParams& p) {
   return s;
 }
 
-}  // namespace
-
-namespace {
-
-template <int NC, bool SCALED, int WPB>
-void launch_bf16_ncsw(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
-  if (streaming)
-    hipLaunchKernelGGL((dispatch_bf16_kernel<NC, kAuxDefault, kAuxNT, SCALED, WPB>), dim3(s.blocks), dim3(64 * WPB),
-                       0, stream, p, s.wpt, s.cpw, s.nchunks);
-  else
-    hipLaunchKernelGGL((dispatch_bf16_kernel<NC, kAuxDefault, kAuxDefault, SCALED, WPB>), dim3(s.blocks),
-                       dim3(64 * WPB), 0, stream, p, s.wpt, s.cpw, s.nchunks);
-}
-
-template <int NC, bool SCALED>
-void launch_bf16_ncs(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
-  if (s.budget)
-    launch_bf16_ncsw<NC, SCALED, kBudgetWaves>(s, p, streaming, stream);
-  else
-    launch_bf16_ncsw<NC, SCALED, kWavesPerBlock>(s, p, streaming, stream);
-}
-
-template <int NC>
-void launch_bf16_nc(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
-  if (p.weights)
-    launch_bf16_ncs<NC, true>(s, p, streaming, stream);
-  else
-    launch_bf16_ncs<NC, false>(s, p, streaming, stream);
-}
-
-template <int NC, int WPB>
-void launch_fp8_ncw(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
-  if (streaming)
-    hipLaunchKernelGGL((dispatch_fp8_kernel<NC, kAuxDefault, kAuxNT, WPB>), dim3(s.blocks), dim3(64 * WPB), 0, stream,
-                       p, s.wpt, s.cpw, s.nchunks);
-  else
-    hipLaunchKernelGGL((dispatch_fp8_kernel<NC, kAuxDefault, kAuxDefault, WPB>), dim3(s.blocks), dim3(64 * WPB), 0,
-                       stream, p, s.wpt, s.cpw, s.nchunks);
-}
-
-template <int NC, int WPB, int ELEM>
-void launch_mx_ncw(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
-  if (streaming)
-    hipLaunchKernelGGL((dispatch_mx_kernel<NC, kAuxDefault, kAuxNT, WPB, ELEM>), dim3(s.blocks), dim3(64 * WPB), 0,
-                       stream, p, s.wpt, s.cpw, s.nchunks);
-  else
-    hipLaunchKernelGGL((dispatch_mx_kernel<NC, kAuxDefault, kAuxDefault, WPB, ELEM>), dim3(s.blocks),
-                       dim3(64 * WPB), 0, stream, p, s.wpt, s.cpw, s.nchunks);
-}
-
-template <int NC, int ELEM>
-void launch_mx_nce(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
-  if (s.budget)
-    launch_mx_ncw<NC, kBudgetWaves, ELEM>(s, p, streaming, stream);
-  else
-    launch_mx_ncw<NC, kWavesPerBlock, ELEM>(s, p, streaming, stream);
-}
-
-template <int NC>
-void launch_mx8_nc(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
-  launch_mx_nce<NC, 8>(s, p, streaming, stream);
-}
-
-template <int NC>
-void launch_mx4_nc(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
-  launch_mx_nce<NC, 4>(s, p, streaming, stream);
-}
-
-template <int NC, int WPB>
-void launch_pq_ncw(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
-  if (streaming)
-    hipLaunchKernelGGL((dispatch_prequantized_kernel<NC, kAuxDefault, kAuxNT, WPB>), dim3(s.blocks), dim3(64 * WPB),
-                       0, stream, p, s.wpt, s.cpw, s.nchunks);
-  else
-    hipLaunchKernelGGL((dispatch_prequantized_kernel<NC, kAuxDefault, kAuxDefault, WPB>), dim3(s.blocks),
-                       dim3(64 * WPB), 0, stream, p, s.wpt, s.cpw, s.nchunks);
-}
-
-template <int NC>
-void launch_pq_nc(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
-  if (s.budget)
-    launch_pq_ncw<NC, kBudgetWaves>(s, p, streaming, stream);
-  else
-    launch_pq_ncw<NC, kWavesPerBlock>(s, p, streaming, stream);
-}
-
-template <int NC>
-void launch_fp8_nc(const Split& s, const RowParams& p, bool streaming, hipStream_t stream) {
-  if (s.budget)
-    launch_fp8_ncw<NC, kBudgetWaves>(s, p, streaming, stream);
-  else
-    launch_fp8_ncw<NC, kWavesPerBlock>(s, p, streaming, stream);
-}
-
-}  // namespace
-
 // The instantiation's chunk capacity equals the (even) chunks per wavefront,
 // so no slice carries dead registers or instructions.
 #define EP_BY_CAPACITY(FN, s, ...)                  \
@@ -565,7 +424,7 @@ void launch_fp8_nc(const Split& s, const RowParams& p, bool streaming, hipStream
 
 hipError_t launch_dispatch_bf16(const RowParams& p, hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
-  const Split s = split_for(p);
+  const DispatchSplit s = dispatch_split(p);
   const bool streaming = (int64_t)p.T * p.k * p.H * 2 >= kStreamingBytes;
   EP_BY_CAPACITY(launch_bf16_nc, s, p, streaming, stream);
   return hipGetLastError();
@@ -573,7 +432,7 @@ hipError_t launch_dispatch_bf16(const RowParams& p, hipStream_t stream) {
 
 hipError_t launch_dispatch_fp8(const RowParams& p, hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
-  const Split s = split_for(p);
+  const DispatchSplit s = dispatch_split(p);
   const bool streaming = (int64_t)p.T * p.k * p.H >= kStreamingBytes;
   EP_BY_CAPACITY(launch_fp8_nc, s, p, streaming, stream);
   return hipGetLastError();
@@ -581,7 +440,7 @@ hipError_t launch_dispatch_fp8(const RowParams& p, hipStream_t stream) {
 
 hipError_t launch_dispatch_mx(const RowParams& p, int elem_bits, hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
-  const Split s = split_for(p);
+  const DispatchSplit s = dispatch_split(p);
   const bool streaming = (int64_t)p.T * p.k * p.H * elem_bits / 8 >= kStreamingBytes;
   if (elem_bits == 8) {
     EP_BY_CAPACITY(launch_mx8_nc, s, p, streaming, stream);
@@ -595,7 +454,7 @@ hipError_t launch_dispatch_prequantized(const RowParams& p_in, hipStream_t strea
   if (p_in.T == 0) return hipSuccess;
   RowParams p = p_in;
   p.H = p_in.H / 2;  // code rows as two-byte columns
-  const Split s = split_for(p);
+  const DispatchSplit s = dispatch_split(p);
   const bool streaming = (int64_t)p.T * p.k * p_in.H >= kStreamingBytes;
   EP_BY_CAPACITY(launch_pq_nc, s, p, streaming, stream);
   return hipGetLastError();

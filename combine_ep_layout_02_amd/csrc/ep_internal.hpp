@@ -39,6 +39,7 @@ struct LayoutPlan {
 };
 
 LayoutPlan plan_layout(int T, int k, int E, int R);
+void prepare_layout_params(const LayoutPlan& plan, LayoutParams& p);  // tile shape and division constants
 hipError_t launch_layout(const LayoutPlan& plan, LayoutParams p, hipStream_t stream);
 
 struct RowParams {
@@ -75,10 +76,23 @@ constexpr int kBudgetWaves = 16;
 // Upper bound of num_topk (the C ABI's EP_MAX_TOPK), for LDS sizing.
 constexpr int kMaxTopk = 64;
 
+// Dispatch work split: wavefronts per token (wpt) and even chunks per
+// wavefront (cpw) for hidden size H, and the launch shape.
+struct DispatchSplit {
+  int nchunks, wpt, cpw, blocks;
+  bool budget;  // persistent kBudgetWaves-wavefront workgroups, one per CU of the budget
+};
+DispatchSplit dispatch_split(const RowParams& p);
+
 hipError_t launch_dispatch_bf16(const RowParams& p, hipStream_t stream);  // weights non-null: scaled copies
 hipError_t launch_dispatch_fp8(const RowParams& p, hipStream_t stream);
 hipError_t launch_dispatch_mx(const RowParams& p, int elem_bits, hipStream_t stream);  // 8: MXFP8, 4: MXFP4
 hipError_t launch_dispatch_prequantized(const RowParams& p, hipStream_t stream);     // src = E4M3 codes
+// Layout and BF16 / FP8 dispatch in one launch when the batch is one layout
+// tile of 16 windows (see ep_layout_dispatch.hip).
+bool layout_dispatch_fusable(const LayoutPlan& plan);
+hipError_t launch_layout_dispatch(const LayoutPlan& plan, LayoutParams lp, const RowParams& rp, bool fp8,
+                                  hipStream_t stream);
 hipError_t launch_combine(const RowParams& p, hipStream_t stream);  // weights null: unit weights
 hipError_t launch_combine_backward(const BackParams& p, hipStream_t stream);
 

@@ -29,7 +29,8 @@ EP_MAX_EXPERTS = 2048
 EP_MAX_TOPK = 64
 EP_MAX_NUM_CUS = 65535
 
-EXPORTED = ("ep_recv_rows", "ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_dispatch_prequantized",
+EXPORTED = ("ep_recv_rows", "ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_layout_dispatch",
+            "ep_dispatch_prequantized",
             "ep_combine", "ep_dispatch_backward", "ep_combine_backward", "ep_status_string", "ep_abi_version",
             "ep_last_hip_error", "ep_check_cvt_e4m3", "ep_check_cvt_bf16", "ep_check_cvt_e2m1")
 
@@ -107,6 +108,8 @@ def lib() -> ctypes.CDLL:
         L.ep_layout.argtypes = [sp] + [vp] * 9 + [ctypes.c_size_t, vp]
         L.ep_dispatch.restype = st
         L.ep_dispatch.argtypes = [sp, vp, vp, ctypes.c_int, vp, vp, vp]
+        L.ep_layout_dispatch.restype = st
+        L.ep_layout_dispatch.argtypes = [sp] + [vp] * 9 + [ctypes.c_size_t, vp, ctypes.c_int, vp, vp, vp]
         L.ep_dispatch_prequantized.restype = st
         L.ep_dispatch_prequantized.argtypes = [sp, vp, vp, vp, vp, vp, vp]
         L.ep_combine.restype = st
@@ -183,6 +186,35 @@ def ep_layout_workspace_bytes(shape: EpShape) -> int:
     out = ctypes.c_size_t()
     _check("ep_layout_workspace_bytes", lib().ep_layout_workspace_bytes(ctypes.byref(shape.c()), ctypes.byref(out)))
     return out.value
+
+
+def _layout_args(shape: EpShape, topk_idx, expert_count, expert_offset, rank_count, rank_offset, slot,
+                 src_pair, diag, workspace):
+    """(shape, 9 pointers, workspace bytes) of ep_layout, checked."""
+    T, k, E, R = shape.num_tokens, shape.num_topk, shape.num_experts, shape.num_ranks
+    rows, ws_bytes = shape.recv_rows, shape.workspace_bytes
+    i32 = torch.int32
+    args = (
+        _ptr(topk_idx, "topk_idx", i32, T * k, optional=T == 0),
+        _ptr(expert_count, "expert_count", i32, E), _ptr(expert_offset, "expert_offset", i32, E + 1),
+        _ptr(rank_count, "rank_count", i32, R), _ptr(rank_offset, "rank_offset", i32, R + 1),
+        _ptr(slot, "slot", i32, T * k, optional=T == 0),
+        _ptr(src_pair, "src_pair", i32, rows, optional=True), _ptr(diag, "diag", i32, 2, optional=True),
+        _ptr(workspace, "workspace", None, None),
+    )
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < ws_bytes:
+        raise ValueError(f"workspace has {nbytes} bytes, needs {ws_bytes}")
+    return (shape.c_ref, *args, nbytes)
+
+
+def ep_layout_dispatch(shape: EpShape, topk_idx, expert_count, expert_offset, rank_count, rank_offset, slot,
+                       src_pair, diag, workspace, x, recv_dtype: int, recv_x, recv_scale=None, stream=None) -> None:
+    """ep_layout then ep_dispatch; one launch for single-tile batches (the decode shape)."""
+    largs = _layout_args(shape, topk_idx, expert_count, expert_offset, rank_count, rank_offset, slot, src_pair,
+                         diag, workspace)
+    dargs = _dispatch_args(shape, x, slot, recv_dtype, recv_x, recv_scale)
+    _check("ep_layout_dispatch", lib().ep_layout_dispatch(*largs, *dargs[1:2], *dargs[3:], _stream(stream)))
 
 
 def ep_layout(shape: EpShape, topk_idx, expert_count, expert_offset, rank_count, rank_offset, slot,
@@ -345,22 +377,18 @@ class Prepared:
 
 def prepare_layout(shape: EpShape, topk_idx, expert_count, expert_offset, rank_count, rank_offset, slot,
                    src_pair=None, diag=None, workspace=None, stream=None) -> Prepared:
-    T, k, E, R = shape.num_tokens, shape.num_topk, shape.num_experts, shape.num_ranks
-    rows, ws_bytes = shape.recv_rows, shape.workspace_bytes
-    i32 = torch.int32
-    args = (
-        _ptr(topk_idx, "topk_idx", i32, T * k, optional=T == 0),
-        _ptr(expert_count, "expert_count", i32, E), _ptr(expert_offset, "expert_offset", i32, E + 1),
-        _ptr(rank_count, "rank_count", i32, R), _ptr(rank_offset, "rank_offset", i32, R + 1),
-        _ptr(slot, "slot", i32, T * k, optional=T == 0),
-        _ptr(src_pair, "src_pair", i32, rows, optional=True), _ptr(diag, "diag", i32, 2, optional=True),
-        _ptr(workspace, "workspace", None, None),
-    )
-    nbytes = workspace.numel() * workspace.element_size()
-    if nbytes < ws_bytes:
-        raise ValueError(f"workspace has {nbytes} bytes, needs {ws_bytes}")
     keep = (topk_idx, expert_count, expert_offset, rank_count, rank_offset, slot, src_pair, diag, workspace)
-    return Prepared("ep_layout", lib().ep_layout, (shape.c_ref, *args, nbytes), keep, stream)
+    return Prepared("ep_layout", lib().ep_layout, _layout_args(shape, *keep), keep, stream)
+
+
+def prepare_layout_dispatch(shape: EpShape, topk_idx, expert_count, expert_offset, rank_count, rank_offset, slot,
+                            src_pair, diag, workspace, x, recv_dtype: int, recv_x, recv_scale=None,
+                            stream=None) -> Prepared:
+    lkeep = (topk_idx, expert_count, expert_offset, rank_count, rank_offset, slot, src_pair, diag, workspace)
+    largs = _layout_args(shape, *lkeep)
+    dargs = _dispatch_args(shape, x, slot, recv_dtype, recv_x, recv_scale)
+    return Prepared("ep_layout_dispatch", lib().ep_layout_dispatch, (*largs, dargs[1], *dargs[3:]),
+                    (*lkeep, x, recv_x, recv_scale), stream)
 
 
 def prepare_dispatch(shape: EpShape, x, slot, recv_dtype: int, recv_x, recv_scale=None, stream=None) -> Prepared:
@@ -428,6 +456,20 @@ class LayoutBuffers:
         ep_layout(self.shape, topk_idx, self.expert_count, self.expert_offset, self.rank_count,
                   self.rank_offset, self.slot, self.src_pair, self.diag, self.workspace, stream)
         return self
+
+    def run_dispatch(self, topk_idx: torch.Tensor, x, recv_dtype: int, recv_x, recv_scale=None,
+                     stream=None) -> "LayoutBuffers":
+        """Layout and dispatch in one call (one launch for single-tile batches)."""
+        ep_layout_dispatch(self.shape, topk_idx, self.expert_count, self.expert_offset, self.rank_count,
+                           self.rank_offset, self.slot, self.src_pair, self.diag, self.workspace, x, recv_dtype,
+                           recv_x, recv_scale, stream)
+        return self
+
+    def prepare_dispatch(self, topk_idx: torch.Tensor, x, recv_dtype: int, recv_x, recv_scale=None,
+                         stream=None) -> Prepared:
+        return prepare_layout_dispatch(self.shape, topk_idx, self.expert_count, self.expert_offset, self.rank_count,
+                                       self.rank_offset, self.slot, self.src_pair, self.diag, self.workspace, x,
+                                       recv_dtype, recv_x, recv_scale, stream)
 
     def prepare(self, topk_idx: torch.Tensor, stream=None) -> Prepared:
         return prepare_layout(self.shape, topk_idx, self.expert_count, self.expert_offset, self.rank_count,

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 4
+#define EP_ABI_VERSION 5
 
 /* Limits checked by every entry point (EP_ERR_UNSUPPORTED beyond them). */
 #define EP_MAX_EXPERTS 2048
@@ -203,6 +203,25 @@ ep_status_t ep_layout(const ep_shape_t *shape, const int32_t *topk_idx,
 ep_status_t ep_dispatch(const ep_shape_t *shape, const void *x, const int32_t *slot,
                         ep_dtype_t recv_dtype, void *recv_x, void *recv_scale,
                         hipStream_t stream);
+
+/*
+ * ep_layout followed by ep_dispatch, with the same arguments and bit for bit
+ * the same results.  When the batch fits one layout tile (T * k <= 1024
+ * pairs with E <= 256; the decode shape) and recv_dtype is EP_BF16 or
+ * EP_FP8_E4M3 and num_cus is 0, it is one launch: every workgroup of the
+ * dispatch rebuilds the (small) layout in LDS while its token loads are in
+ * flight, instead of waiting for a layout launch and reading the slots back
+ * (the per-step layout of the decode path: [DOC] item 3; [GN] "Patrones de
+ * uso en entrenamiento, prefill y decoding").  Otherwise it enqueues the
+ * two calls.  Argument checks are those of the two calls.
+ */
+ep_status_t ep_layout_dispatch(const ep_shape_t *shape, const int32_t *topk_idx,
+                               int32_t *expert_count, int32_t *expert_offset,
+                               int32_t *rank_count, int32_t *rank_offset,
+                               int32_t *slot, int32_t *src_pair, int32_t *diag,
+                               void *workspace, size_t workspace_bytes,
+                               const void *x, ep_dtype_t recv_dtype, void *recv_x,
+                               void *recv_scale, hipStream_t stream);
 
 /*
  * Dispatch of tokens the caller has already quantised: DeepEP's dispatch

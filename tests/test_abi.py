@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_abi_version_and_status_strings(L):
     header = open(HEADER).read()
-    assert ep.ep_abi_version() == int(re.search(r"#define EP_ABI_VERSION (\d+)", header).group(1)) == 4
+    assert ep.ep_abi_version() == int(re.search(r"#define EP_ABI_VERSION (\d+)", header).group(1)) == 5
     for code in range(6):
         s = ep.ep_status_string(code)
         assert s.startswith("EP_"), s
@@ -120,6 +120,7 @@ def test_bad_shapes_rejected(L, kw, code):
     assert L.ep_layout(ctypes.byref(shape_c(**kw)), *([None] * 9), 0, None) == code
     assert L.ep_dispatch(ctypes.byref(shape_c(**kw)), None, None, 0, None, None, None) == code
     assert L.ep_dispatch_prequantized(ctypes.byref(shape_c(**kw)), *([None] * 5), None) == code
+    assert L.ep_layout_dispatch(ctypes.byref(shape_c(**kw)), *([None] * 9), 0, None, 0, None, None, None) == code
     assert L.ep_combine(ctypes.byref(shape_c(**kw)), None, None, None, None, None) == code
     assert L.ep_dispatch_backward(ctypes.byref(shape_c(**kw)), None, None, None, None) == code
     assert L.ep_combine_backward(ctypes.byref(shape_c(**kw)), *([None] * 6), None) == code
@@ -181,6 +182,23 @@ def test_mx_dispatch_argument_checks(L):
         assert L.ep_dispatch(ctypes.byref(shape_c(num_tokens=0)), None, None, dt, None, None, None) == OK
     assert L.ep_dispatch(s, FAKE, FAKE, 4, FAKE, FAKE, None) == INVALID               # no dtype 4
     assert L.ep_dispatch(ctypes.byref(shape_c(hidden=160)), FAKE, FAKE, 1, FAKE, FAKE, None) == UNSUPPORTED
+
+
+def test_layout_dispatch_argument_checks(L):
+    s = ctypes.byref(shape_c())
+    ws = ctypes.c_size_t()
+    assert L.ep_layout_workspace_bytes(s, ctypes.byref(ws)) == OK
+    lay = [FAKE] * 8
+    # layout side: missing output, workspace too small
+    q = list(lay)
+    q[1] = None
+    assert L.ep_layout_dispatch(s, *q, FAKE, ws.value, FAKE, 1, FAKE, FAKE, None) == INVALID
+    assert L.ep_layout_dispatch(s, *lay, FAKE, ws.value - 1, FAKE, 1, FAKE, FAKE, None) == WORKSPACE
+    # dispatch side: x missing, bad dtype, FP8 without scales, misaligned recv_x
+    assert L.ep_layout_dispatch(s, *lay, FAKE, ws.value, None, 1, FAKE, FAKE, None) == INVALID
+    assert L.ep_layout_dispatch(s, *lay, FAKE, ws.value, FAKE, 9, FAKE, FAKE, None) == INVALID
+    assert L.ep_layout_dispatch(s, *lay, FAKE, ws.value, FAKE, 1, FAKE, None, None) == INVALID
+    assert L.ep_layout_dispatch(s, *lay, FAKE, ws.value, FAKE, 0, FAKE + 4, None, None) == MISALIGNED
 
 
 def test_prequantized_dispatch_argument_checks(L):

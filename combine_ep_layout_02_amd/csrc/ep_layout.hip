@@ -201,8 +201,9 @@ __global__ __launch_bounds__(1024) void layout_finalize_kernel(LayoutParams p) {
 // host side
 // ---------------------------------------------------------------------------
 
-// ceil(2^32 / d): for n * d < 2^32, n / d == (n * magic) >> 32.
-uint32_t magic_for(uint32_t d) { return (uint32_t)(0xFFFFFFFFull / d + 1ull); }
+// ceil(2^32 / d): for n * d < 2^32, n / d == (n * magic) >> 32.  For d = 1
+// that is 2^32, which does not fit: 0 stands for it (udiv returns n).
+uint32_t magic_for(uint32_t d) { return d == 1 ? 0u : (uint32_t)(0xFFFFFFFFull / d + 1ull); }
 
 }  // namespace
 

@@ -11,7 +11,11 @@ namespace lay {
 
 static __device__ __forceinline__ int aligned_count(int c, int A) { return ((c + A - 1) / A) * A; }
 
-static __device__ __forceinline__ int udiv(uint32_t n, uint32_t magic) { return (int)__umulhi(n, magic); }
+// n / d from magic = ceil(2^32 / d) (exact for n * d < 2^32); d = 1 has no
+// 32-bit magic and is encoded as 0.
+static __device__ __forceinline__ int udiv(uint32_t n, uint32_t magic) {
+  return magic ? (int)__umulhi(n, magic) : (int)n;
+}
 
 // Inclusive prefix sum over the 64 lanes of a wavefront with DPP: four
 // row_shr steps scan each 16-lane row, then two row broadcasts carry row

@@ -155,6 +155,13 @@ LAYOUT_EDGE = [
     # more tiles than can be resident at once: the two-kernel path
     ("too_many_tiles_for_one_launch", 70000, 8, 256, 8, 1, 0, 0.01, 0.0, None),
     ("padded_multitile", 3000, 8, 64, 8, 1, 200, 0.0, 0.0, None),
+    # divisors of 1 (k, E / R, R, E): the multiply-high division's special case
+    ("k1_one_tile", 300, 1, 8, 2, 1, 0, 0.0, 0.0, None),
+    ("k1_multitile", 5000, 1, 16, 4, 1, 0, 0.05, 0.0, None),
+    ("one_rank_multitile", 3000, 4, 16, 1, 1, 0, 0.0, 0.0, None),
+    ("one_expert_per_rank", 2000, 2, 8, 8, 1, 0, 0.0, 0.0, None),
+    ("one_expert_multitile", 3000, 1, 1, 1, 1, 0, 0.0, 0.0, None),
+    ("one_expert_per_rank_r128", 900, 4, 128, 128, 1, 0, 0.0, 0.0, None),
 ]
 
 

@@ -164,6 +164,7 @@ def time_steps(step, steps, warmup, fused=False):
     for _ in range(steps):
         run()
     end.record()
+    step.submit_s = time.perf_counter() - t0   # host time to enqueue the steps
     torch.cuda.synchronize()
     return start.elapsed_time(end), time.perf_counter() - t0
 
@@ -555,10 +556,12 @@ def main():
         dstep = Step(wl.WORKLOADS["decode"], dev, fp8=True)
         n = 500
         d_total, _ = time_steps(dstep, n, 50, fused=True)
+        d_submit = dstep.submit_s
         d_unfused, _ = time_steps(dstep, n, 50)
         d_stage = time_stages(dstep, 100)
         dec = {"us_per_call": round(d_total / n * 1e3, 2),
                "us_per_call_separate_layout": round(d_unfused / n * 1e3, 2),
+               "host_enqueue_us_per_call": round(d_submit / n * 1e6, 2),
                "layout_us": round(float(np.median(d_stage[:, 0])) * 1e3, 2),
                "dispatch_us": round(float(np.median(d_stage[:, 1])) * 1e3, 2),
                "combine_us": round(float(np.median(d_stage[:, 2])) * 1e3, 2),

@@ -26,14 +26,11 @@
 namespace ep {
 namespace {
 
-// 16-byte column groups per lane per row: the work unit covers 512 * groups
-// columns.
-#ifndef EP_COMBINE_GROUPS
-#define EP_COMBINE_GROUPS 2
-#endif
-
-constexpr int kGroups = EP_COMBINE_GROUPS;
-constexpr int kChunk = 512 * kGroups;
+// 16-byte column groups per lane per row (NG): a work item covers 512 * NG
+// columns.  Two groups (1024 columns, 16 loads in flight per wavefront) for
+// large batches; one group for small ones, where twice the wavefronts spread
+// the latency-bound gather over more CUs (128 decode tokens: 3.4 vs 3.7 us).
+constexpr int kSmallItems = 4096;  // (token, 1024-column) items below which NG = 1
 constexpr int kWavesPerBlock = 1;  // whole-GPU launches: 64-thread blocks, measured ~3% faster than 256 at the 8K step
 
 __device__ __forceinline__ void fma8(float* acc, float w, u32x4 v) {
@@ -85,7 +82,7 @@ __device__ __forceinline__ void accumulate(const uint16_t* y, int64_t rows, int 
 // Items (token, chunk) are handed out grid-stride: a whole-GPU launch has one
 // wavefront per item and runs the loop once; a launch limited to a CU budget
 // runs that many persistent workgroups of WPB wavefronts.
-template <int K, int AUX_LD, int AUX_ST, int WPB>
+template <int K, int AUX_LD, int AUX_ST, int WPB, int NG>
 __global__ __launch_bounds__(64 * WPB) void combine_kernel(RowParams p, int chunks) {
   const int lane = threadIdx.x & 63;
   const int items = p.T * chunks;
@@ -95,7 +92,7 @@ __global__ __launch_bounds__(64 * WPB) void combine_kernel(RowParams p, int chun
   const int c = item - t * chunks;
   const int H = p.H;
   const int k = K > 0 ? K : p.k;
-  const uint32_t col0 = (uint32_t)(c * kChunk + lane * 8);
+  const uint32_t col0 = (uint32_t)(c * 512 * NG + lane * 8);
 
   int sl = -1, wl = 0;
   if (lane < k) {
@@ -103,44 +100,50 @@ __global__ __launch_bounds__(64 * WPB) void combine_kernel(RowParams p, int chun
     wl = (int)__float_as_uint(p.weights ? p.weights[(int64_t)t * k + lane] : 1.0f);
   }
   const uint16_t* y = static_cast<const uint16_t*>(p.src);
-  float acc[kGroups][8];
+  float acc[NG][8];
 #pragma unroll
-  for (int g = 0; g < kGroups; ++g)
+  for (int g = 0; g < NG; ++g)
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[g][i] = 0.0f;
 
   if constexpr (K > 0) {
-    accumulate<K, kGroups, AUX_LD>(y, p.rows, H, k, 0, sl, wl, col0, acc);
+    accumulate<K, NG, AUX_LD>(y, p.rows, H, k, 0, sl, wl, col0, acc);
   } else {
-    for (int j0 = 0; j0 < k; j0 += 8) accumulate<8, kGroups, AUX_LD>(y, p.rows, H, k, j0, sl, wl, col0, acc);
+    for (int j0 = 0; j0 < k; j0 += 8) accumulate<8, NG, AUX_LD>(y, p.rows, H, k, j0, sl, wl, col0, acc);
   }
 
   uint16_t* out = static_cast<uint16_t*>(p.dst) + (int64_t)t * H;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, (uint32_t)H * 2u);
 #pragma unroll
-  for (int g = 0; g < kGroups; ++g) store16<AUX_ST>(ro, (col0 + 512u * g) * 2u, pack8(acc[g]));
+  for (int g = 0; g < NG; ++g) store16<AUX_ST>(ro, (col0 + 512u * g) * 2u, pack8(acc[g]));
   }
 }
 
-template <int K, int WPB>
+template <int K, int WPB, int NG>
 void launch_kw(const RowParams& p, int blocks, int chunks, hipStream_t stream) {
   const dim3 block(64 * WPB);
   if ((int64_t)p.T * p.k * p.H * 2 < kStreamingBytes)
-    hipLaunchKernelGGL((combine_kernel<K, kAuxDefault, kAuxDefault, WPB>), dim3(blocks), block, 0, stream, p, chunks);
+    hipLaunchKernelGGL((combine_kernel<K, kAuxDefault, kAuxDefault, WPB, NG>), dim3(blocks), block, 0, stream, p,
+                       chunks);
   else if ((int64_t)p.T * p.H * 2 <= kCacheableOutputBytes)
-    hipLaunchKernelGGL((combine_kernel<K, kAuxNT, kAuxSC1, WPB>), dim3(blocks), block, 0, stream, p, chunks);
+    hipLaunchKernelGGL((combine_kernel<K, kAuxNT, kAuxSC1, WPB, NG>), dim3(blocks), block, 0, stream, p, chunks);
   else
-    hipLaunchKernelGGL((combine_kernel<K, kAuxNT, kAuxNT, WPB>), dim3(blocks), block, 0, stream, p, chunks);
+    hipLaunchKernelGGL((combine_kernel<K, kAuxNT, kAuxNT, WPB, NG>), dim3(blocks), block, 0, stream, p, chunks);
 }
 
 template <int K>
-hipError_t launch_k(const RowParams& p, int chunks, hipStream_t stream) {
-  const int64_t items = (int64_t)p.T * chunks;
+hipError_t launch_k(const RowParams& p, hipStream_t stream) {
+  const int chunks2 = (p.H + 1023) / 1024;
   if (p.num_cus > 0) {
-    const int64_t need = (items + kBudgetWaves - 1) / kBudgetWaves;
-    launch_kw<K, kBudgetWaves>(p, (int)(need < p.num_cus ? need : p.num_cus), chunks, stream);
+    const int64_t need = ((int64_t)p.T * chunks2 + kBudgetWaves - 1) / kBudgetWaves;
+    launch_kw<K, kBudgetWaves, 2>(p, (int)(need < p.num_cus ? need : p.num_cus), chunks2, stream);
+  } else if ((int64_t)p.T * chunks2 < kSmallItems) {
+    const int chunks1 = (p.H + 511) / 512;
+    launch_kw<K, kWavesPerBlock, 1>(p, (int)(((int64_t)p.T * chunks1 + kWavesPerBlock - 1) / kWavesPerBlock),
+                                    chunks1, stream);
   } else {
-    launch_kw<K, kWavesPerBlock>(p, (int)((items + kWavesPerBlock - 1) / kWavesPerBlock), chunks, stream);
+    launch_kw<K, kWavesPerBlock, 2>(p, (int)(((int64_t)p.T * chunks2 + kWavesPerBlock - 1) / kWavesPerBlock),
+                                    chunks2, stream);
   }
   return hipGetLastError();
 }
@@ -149,14 +152,13 @@ hipError_t launch_k(const RowParams& p, int chunks, hipStream_t stream) {
 
 hipError_t launch_combine(const RowParams& p, hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
-  const int chunks = (p.H + kChunk - 1) / kChunk;
   switch (p.k) {
-    case 1: return launch_k<1>(p, chunks, stream);
-    case 2: return launch_k<2>(p, chunks, stream);
-    case 4: return launch_k<4>(p, chunks, stream);
-    case 6: return launch_k<6>(p, chunks, stream);
-    case 8: return launch_k<8>(p, chunks, stream);
-    default: return launch_k<0>(p, chunks, stream);
+    case 1: return launch_k<1>(p, stream);
+    case 2: return launch_k<2>(p, stream);
+    case 4: return launch_k<4>(p, stream);
+    case 6: return launch_k<6>(p, stream);
+    case 8: return launch_k<8>(p, stream);
+    default: return launch_k<0>(p, stream);
   }
 }
 

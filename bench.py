@@ -495,6 +495,34 @@ def cpu_baseline(step):
                       f"median of 2 runs, {t:.2f} s each, single-threaded C on the host"}
 
 
+def cpu_baseline_parallel(step, threads):
+    """The same oracle functions on all the host's cores: the layout (a single
+    sequential counting sort) on one thread, then dispatch and combine on
+    contiguous token ranges, one per thread (ctypes releases the GIL)."""
+    import oracle  # test infrastructure; only this leg of the benchmark uses it
+    from concurrent.futures import ThreadPoolExecutor
+    w, inp = step.w, step.inp
+    T = w.num_tokens
+    q = np.zeros((w.recv_rows, w.hidden), np.uint8)
+    sc = np.zeros((w.recv_rows, w.hidden // 128), np.float32)
+    out = np.zeros((T, w.hidden), np.uint16)
+    bounds = [(T * i // threads, T * (i + 1) // threads) for i in range(threads)]
+    times = []
+    with ThreadPoolExecutor(threads) as pool:
+        for _ in range(3):
+            t0 = time.perf_counter()
+            lay = oracle.layout(inp.topk_idx, w.num_experts, w.num_ranks, w.expert_alignment, w.capacity)
+            list(pool.map(lambda b: oracle.dispatch_fp8(inp.x[b[0]:b[1]], lay.slot[b[0]:b[1]], w.recv_rows, (q, sc)),
+                          bounds))
+            list(pool.map(lambda b: oracle.combine(inp.y, lay.slot[b[0]:b[1]], inp.topk_weights[b[0]:b[1]],
+                                                   out[b[0]:b[1]]), bounds))
+            times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"value": round(step.bytes / t / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the full {w.name} step, layout on one thread, dispatch and combine split by tokens over "
+                      f"{threads} threads, median of 3 runs, {t:.3f} s each"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -585,7 +613,11 @@ def main():
     del flush
 
     copy_gbps = calibration_copy(dev, reps=3 if args.calibration_copy else 5)
-    cb = None if args.no_cpu_baseline else cpu_baseline(step)
+    cb = cbp = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle")
+        cb = cpu_baseline(step)
+        cbp = cpu_baseline_parallel(step, max(1, min(16, len(os.sched_getaffinity(0)))))
 
     comb_bytes = bytes_combine(w)
     achieved = comb_bytes / (comb_ms / 1e3) / 1e9
@@ -631,6 +663,7 @@ def main():
         "dispatch_formats": formats,
         "configs": configs,
         "cpu_baseline": cb,
+        "cpu_baseline_all_cores": cbp,
         "wall_s_timed": round(wall, 4),
     }
     print(json.dumps(result), flush=True)

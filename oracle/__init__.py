@@ -148,25 +148,32 @@ def dispatch_bf16(x: np.ndarray, slot: np.ndarray, rows: int) -> np.ndarray:
     return out
 
 
-def dispatch_fp8(x: np.ndarray, slot: np.ndarray, rows: int):
+def dispatch_fp8(x: np.ndarray, slot: np.ndarray, rows: int, out=None):
+    """FP8 dispatch; `out` = (codes [rows, H] uint8, scales [rows, H/128] fp32) to fill in place
+    (rows no slot of these tokens maps to are left as they are)."""
     x = _c(x, np.uint16)
     slot = _c(slot, np.int32)
     T, H = x.shape
     k = slot.shape[1]
     assert H % 128 == 0
-    q = np.zeros((rows, H), np.uint8)
-    s = np.zeros((rows, H // 128), np.float32)
+    if out is None:
+        out = (np.zeros((rows, H), np.uint8), np.zeros((rows, H // 128), np.float32))
+    q, s = out
+    assert q.flags.c_contiguous and s.flags.c_contiguous and q.shape == (rows, H) and s.shape == (rows, H // 128)
     lib().oracle_dispatch_fp8(T, H, k, _p(x), _p(slot), _p(q), _p(s))
     return q, s
 
 
-def combine(y: np.ndarray, slot: np.ndarray, weights: np.ndarray) -> np.ndarray:
+def combine(y: np.ndarray, slot: np.ndarray, weights: np.ndarray, out=None) -> np.ndarray:
+    """Combine; `out` = a C-contiguous uint16 [T, H] array to fill in place."""
     y = _c(y, np.uint16)
     slot = _c(slot, np.int32)
     w = _c(weights, np.float32)
     T, k = slot.shape
     H = y.shape[1]
-    out = np.zeros((T, H), np.uint16)
+    if out is None:
+        out = np.zeros((T, H), np.uint16)
+    assert out.flags.c_contiguous and out.shape == (T, H) and out.dtype == np.uint16
     lib().oracle_combine(T, H, k, _p(y), _p(slot), _p(w), _p(out))
     return out
 

@@ -27,8 +27,8 @@ runs of this script (FETCH_SIZE, then WRITE_SIZE) with --calibration-copy,
 which adds a plain 1 GiB device copy whose true byte counts scale the
 counters:
 
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d F -- python3 bench.py --steps 3 --warmup 1 --no-decode --no-configs --no-cpu-baseline --calibration-copy
-    rocprofv3 --pmc WRITE_SIZE --output-format csv -d W -- python3 bench.py --steps 3 --warmup 1 --no-decode --no-configs --no-cpu-baseline --calibration-copy
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d F -- python3 bench.py --steps 3 --warmup 1 --no-decode --no-configs --no-extras --no-cpu-baseline --calibration-copy
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d W -- python3 bench.py --steps 3 --warmup 1 --no-decode --no-configs --no-extras --no-cpu-baseline --calibration-copy
     python3 bench.py --traffic-from F W
 
 The last command writes profiles/combine_v3_traffic.json, stamped with a hash
@@ -531,6 +531,8 @@ def main():
     ap.add_argument("--workload", default="v3", choices=["v3", "skew"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the backward pair and the other dispatch formats")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the tiny, mid and 16K-token skewed workloads")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -573,10 +575,12 @@ def main():
     cold_stage = time_stages(step, 20, flush)
     cold_us = float(np.median(cold_step)) * 1e3
 
-    log("[bench] backward pair")
-    backward = time_backward(step, 20)
-    log("[bench] dispatch formats")
-    formats = time_formats(step, 20)
+    backward = formats = None
+    if not args.no_extras:
+        log("[bench] backward pair")
+        backward = time_backward(step, 20)
+        log("[bench] dispatch formats")
+        formats = time_formats(step, 20)
 
     dec = None
     if not args.no_decode:

@@ -189,17 +189,19 @@ def time_stages(step, steps, flush=None):
 
 
 class ReadFlush:
-    """Reads a 1 GiB buffer (a sum into one int64): afterwards the 256 MB
-    Infinity Cache and the L2s hold clean lines of that buffer, none of the
-    step's data, and there is no dirty data whose write-back the next step
-    would pay for (as there would be after writing the buffer)."""
+    """Reads a 1 GiB buffer (an fp32 sum into one value): afterwards the
+    256 MB Infinity Cache and the L2s hold clean lines of that buffer, none
+    of the step's data, and there is no dirty data whose write-back the next
+    step would pay for (as there would be after writing the buffer).  The
+    sum is taken in the buffer's own dtype: asking for another one would
+    first write a converted copy."""
 
     def __init__(self, dev):
-        self.buf = torch.ones(1 << 28, dtype=torch.int32, device=dev)
-        self.sink = torch.empty((), dtype=torch.int64, device=dev)
+        self.buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        self.sink = torch.empty((), dtype=torch.float32, device=dev)
 
     def __call__(self):
-        self.sink.copy_(self.buf.sum(dtype=torch.int64))
+        self.sink.copy_(self.buf.sum())
 
 
 def time_cold(step, reps, flush):

@@ -320,6 +320,14 @@ EP_EXPORT ep_status_t ep_check_cvt_e2m1(const float* in, uint8_t* out, int64_t n
   return hip_status(ep::launch_check_cvt_e2m1(in, out, n, stream));
 }
 
+EP_EXPORT ep_status_t ep_check_quant_e4m3(const uint16_t* x, const float* s, uint8_t* out, int64_t n,
+                                          hipStream_t stream) {
+  if (n < 0) return EP_ERR_INVALID_ARG;
+  if (n > 0 && (!x || !s || !out)) return EP_ERR_INVALID_ARG;
+  if (!aligned(x, 2) || !aligned(s, 4)) return EP_ERR_MISALIGNED;
+  return hip_status(ep::launch_check_quant_e4m3(x, s, out, n, stream));
+}
+
 EP_EXPORT ep_status_t ep_check_cvt_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream) {
   if (n < 0) return EP_ERR_INVALID_ARG;
   if (n > 0 && (!in || !out)) return EP_ERR_INVALID_ARG;

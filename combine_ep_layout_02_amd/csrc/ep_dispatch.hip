@@ -271,6 +271,15 @@ __global__ __launch_bounds__(256) void check_cvt_e4m3_kernel(const float* in, ui
   }
 }
 
+__global__ __launch_bounds__(256) void check_quant_e4m3_kernel(const uint16_t* x, const float* sc, uint8_t* out,
+                                                               int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const float s = sc[i];
+    const float q = quotient_for_e4m3(__uint_as_float((uint32_t)x[i] << 16), s, 1.0f / s);
+    out[i] = (uint8_t)pack_e4m3x4(q, 0.0f, 0.0f, 0.0f);
+  }
+}
+
 __global__ __launch_bounds__(256) void check_cvt_e2m1_kernel(const float* in, uint8_t* out, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     out[i] = (uint8_t)e2m1_code(in[i]);
@@ -467,6 +476,14 @@ hipError_t launch_check_cvt_e4m3(const float* in, uint8_t* out, int64_t n, hipSt
   const int64_t want = (n + 1023) / 1024;
   const int blocks = (int)(want < 65536 ? want : 65536);
   hipLaunchKernelGGL(check_cvt_e4m3_kernel, dim3(blocks), dim3(256), 0, stream, in, out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_quant_e4m3(const uint16_t* x, const float* s, uint8_t* out, int64_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t want = (n + 255) / 256;
+  const int blocks = (int)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(check_quant_e4m3_kernel, dim3(blocks), dim3(256), 0, stream, x, s, out, n);
   return hipGetLastError();
 }
 

@@ -99,5 +99,6 @@ hipError_t launch_combine_backward(const BackParams& p, hipStream_t stream);
 hipError_t launch_check_cvt_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 hipError_t launch_check_cvt_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream);
 hipError_t launch_check_cvt_e2m1(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
+hipError_t launch_check_quant_e4m3(const uint16_t* x, const float* s, uint8_t* out, int64_t n, hipStream_t stream);
 
 }  // namespace ep

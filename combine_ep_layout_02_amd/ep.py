@@ -32,7 +32,8 @@ EP_MAX_NUM_CUS = 65535
 EXPORTED = ("ep_recv_rows", "ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_layout_dispatch",
             "ep_dispatch_prequantized",
             "ep_combine", "ep_dispatch_backward", "ep_combine_backward", "ep_status_string", "ep_abi_version",
-            "ep_last_hip_error", "ep_check_cvt_e4m3", "ep_check_cvt_bf16", "ep_check_cvt_e2m1")
+            "ep_last_hip_error", "ep_check_cvt_e4m3", "ep_check_cvt_bf16", "ep_check_cvt_e2m1",
+            "ep_check_quant_e4m3")
 
 
 class EpError(RuntimeError):
@@ -120,6 +121,8 @@ def lib() -> ctypes.CDLL:
         L.ep_combine_backward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp]
         L.ep_check_cvt_e4m3.restype = st
         L.ep_check_cvt_e4m3.argtypes = [vp, vp, ctypes.c_int64, vp]
+        L.ep_check_quant_e4m3.restype = st
+        L.ep_check_quant_e4m3.argtypes = [vp, vp, vp, ctypes.c_int64, vp]
         L.ep_check_cvt_e2m1.restype = st
         L.ep_check_cvt_e2m1.argtypes = [vp, vp, ctypes.c_int64, vp]
         L.ep_check_cvt_bf16.restype = st
@@ -333,6 +336,13 @@ def ep_check_cvt_e4m3(inp, out, stream=None) -> None:
     _check("ep_check_cvt_e4m3", lib().ep_check_cvt_e4m3(
         _ptr(inp, "in", torch.float32, n, optional=n == 0), _ptr(out, "out", _BYTE_LIKE, n, optional=n == 0),
         n, _stream(stream)))
+
+
+def ep_check_quant_e4m3(x, s, out, stream=None) -> None:
+    n = x.numel()
+    _check("ep_check_quant_e4m3", lib().ep_check_quant_e4m3(
+        _ptr(x, "x", _BF16_LIKE, n, optional=n == 0), _ptr(s, "s", torch.float32, n, optional=n == 0),
+        _ptr(out, "out", _BYTE_LIKE, n, optional=n == 0), n, _stream(stream)))
 
 
 def ep_check_cvt_e2m1(inp, out, stream=None) -> None:

@@ -322,12 +322,21 @@ int ep_last_hip_error(void);
  *   ep_check_cvt_bf16: out[i] = BF16_RNE(in[i]) for finite in[i]
  *   ep_check_cvt_e2m1: out[i] = E2M1 code (low 4 bits) of in[i], nearest
  *                      with ties to even, saturating at +-6, sign kept
- * in is a device fp32 array of n elements, out a device array of n codes
- * (uint8) or BF16 bit patterns (uint16); n >= 0.
+ *   ep_check_quant_e4m3: out[i] = the E4M3 code FP8 dispatch stores for the
+ *                      BF16 value x[i] (bit pattern) under block scale s[i]:
+ *                      the code of the correctly rounded quotient x / s,
+ *                      through the dispatch kernels' own quotient routine;
+ *                      defined for |x| <= 448 * s (every value a block with
+ *                      that scale holds)
+ * in is a device fp32 array of n elements (x: n BF16 bit patterns and s: n
+ * fp32 scales), out a device array of n codes (uint8) or BF16 bit patterns
+ * (uint16); n >= 0.
  */
 ep_status_t ep_check_cvt_e4m3(const float *in, uint8_t *out, int64_t n, hipStream_t stream);
 ep_status_t ep_check_cvt_bf16(const float *in, uint16_t *out, int64_t n, hipStream_t stream);
 ep_status_t ep_check_cvt_e2m1(const float *in, uint8_t *out, int64_t n, hipStream_t stream);
+ep_status_t ep_check_quant_e4m3(const uint16_t *x, const float *s, uint8_t *out, int64_t n,
+                                hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -57,6 +57,7 @@ def lib():
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
         L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
         L.oracle_e4m3_encode_array.argtypes = [vp, vp, i64]
+        L.oracle_fp8_quantize_array.argtypes = [vp, vp, vp, i64]
         L.oracle_dispatch_bf16.argtypes = [i64, i64, i64, vp, vp, vp]
         L.oracle_dispatch_fp8.argtypes = [i64, i64, i64, vp, vp, vp, vp]
         L.oracle_combine.argtypes = [i64, i64, i64, vp, vp, vp, vp]
@@ -246,3 +247,12 @@ def dispatch_mx(x: np.ndarray, slot: np.ndarray, rows: int, elem_bits: int):
     s = np.zeros((rows, H // 32), np.uint8)
     lib().oracle_dispatch_mx(T, H, k, elem_bits, _p(x), _p(slot), _p(q), _p(s))
     return q, s
+
+
+def fp8_quantize(x_bits: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """E4M3 code of each BF16 value x (bits) over its fp32 block scale s (FP8 dispatch's step)."""
+    x = _c(x_bits, np.uint16)
+    s = _c(s, np.float32)
+    out = np.empty(x.shape, np.uint8)
+    lib().oracle_fp8_quantize_array(_p(x), _p(s), _p(out), x.size)
+    return out

@@ -278,6 +278,14 @@ void oracle_e4m3_encode_array(const float *in, uint8_t *out, int64_t n)
     for (i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(in[i]);
 }
 
+/* The FP8 dispatch's per-element step (R8) on its own: code of the BF16
+ * value x[i] divided by the block scale s[i] (one fp32 division). */
+void oracle_fp8_quantize_array(const uint16_t *x, const float *s, uint8_t *out, int64_t n)
+{
+    int64_t i;
+    for (i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(bf16_to_f32(x[i]) / s[i]);
+}
+
 /* ------------------------------------------------------------------ */
 /* Dispatch                                                            */
 /* ------------------------------------------------------------------ */

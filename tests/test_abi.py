@@ -267,6 +267,10 @@ def test_check_helpers_argument_checks(L):
     assert L.ep_check_cvt_e2m1(None, None, -1, None) == INVALID
     assert L.ep_check_cvt_e2m1(FAKE + 1, FAKE, 4, None) == MISALIGNED
     assert L.ep_check_cvt_e2m1(None, None, 0, None) == OK
+    assert L.ep_check_quant_e4m3(None, FAKE, FAKE, 4, None) == INVALID
+    assert L.ep_check_quant_e4m3(FAKE + 1, FAKE, FAKE, 4, None) == MISALIGNED
+    assert L.ep_check_quant_e4m3(FAKE, FAKE + 2, FAKE, 4, None) == MISALIGNED
+    assert L.ep_check_quant_e4m3(None, None, None, 0, None) == OK
 
 
 def test_binding_rejects_host_tensors():

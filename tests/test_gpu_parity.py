@@ -387,6 +387,41 @@ def test_e4m3_conversion_exhaustive():
     assert bad == 0
 
 
+def test_fp8_quantiser_exhaustive():
+    """Every pair (block amax, BF16 x) with 0 < amax finite and |x| <= amax, both signs of x
+    (~1.07e9 pairs): the dispatch kernels' quotient routine (a multiplication by 1/s, with
+    the division taken near E4M3 rounding thresholds) gives the oracle's code of x / s."""
+    amax = np.arange(1, 0x7F80, dtype=np.int64)          # positive finite BF16 magnitudes
+    s_of = (np.maximum(wl.bf16_bits_to_f32(amax.astype(np.uint16)), np.float32(1e-4)) /
+            np.float32(448.0)).astype(np.float32)        # block scale per amax (fp32, as the oracle)
+    counts = 2 * (amax + 1)                                # x in [0, amax] and [-amax, -0]
+    pool = ThreadPoolExecutor(16)
+    bad, total, a0 = 0, 0, 0
+    out = torch.empty(1 << 27, dtype=torch.uint8, device=DEV)
+    while a0 < len(amax):
+        a1 = a0
+        n = 0
+        while a1 < len(amax) and n + counts[a1] <= (1 << 27):
+            n += int(counts[a1])
+            a1 += 1
+        c = counts[a0:a1]
+        start = np.repeat(np.cumsum(c) - c, c)
+        p = np.arange(n, dtype=np.int64) - start
+        am = np.repeat(amax[a0:a1], c)
+        x = np.where(p <= am, p, 0x8000 | (p - am - 1)).astype(np.uint16)
+        s = np.repeat(s_of[a0:a1], c)
+        ep.ep_check_quant_e4m3(torch.from_numpy(x.view(np.int16)).to(DEV), torch.from_numpy(s).to(DEV), out[:n])
+        got = out[:n].cpu().numpy()
+        parts = np.array_split(np.arange(n), 16)
+        want = np.concatenate(list(pool.map(lambda ix: oracle.fp8_quantize(x[ix], s[ix]), parts)))
+        bad += int((got != want).sum())
+        total += n
+        a0 = a1
+    pool.shutdown()
+    log(f"[quant-e4m3] {total} pairs, {bad} mismatches")
+    assert total == int(counts.sum()) and bad == 0
+
+
 def test_bf16_conversion_sweep():
     rng = np.random.default_rng(17)
     bits = rng.integers(0, 1 << 32, 1 << 25, dtype=np.uint64).astype(np.uint32)

@@ -541,6 +541,20 @@ def test_dispatch_backward_k1_is_gather_and_within_bound():
     assert (np.abs(gx - exact) <= half_ulp + k * 2.0 ** -24 * np.abs(Gf[slot]).sum(1) + 1e-45).all()
 
 
+def test_fp8_quantize_array_is_the_dispatch_step():
+    """The per-element quantiser equals the FP8 dispatch's codes under the dispatch's own
+    block scales, and agrees with torch's float8_e4m3fn cast of the fp32 quotient."""
+    w = wl.WORKLOADS["tiny"]
+    inp = wl.make_inputs(w, with_y=False)
+    T, H = inp.x.shape
+    q, sc = oracle.dispatch_fp8(inp.x, np.arange(T, dtype=np.int32)[:, None], T)
+    s_el = np.repeat(sc, 128, axis=1)
+    got = oracle.fp8_quantize(inp.x, s_el)
+    assert np.array_equal(got, q)
+    quot = (torch.from_numpy(wl.bf16_bits_to_f32(inp.x)) / torch.from_numpy(s_el)).numpy()
+    assert np.array_equal(got, _torch_e4m3(quot))
+
+
 # --------------------------------------------------------------------------
 # other dispatch precisions: pre-quantised FP8, MXFP8, MXFP4
 # --------------------------------------------------------------------------

@@ -274,9 +274,8 @@ __global__ __launch_bounds__(256) void check_cvt_e4m3_kernel(const float* in, ui
 __global__ __launch_bounds__(256) void check_quant_e4m3_kernel(const uint16_t* x, const float* sc, uint8_t* out,
                                                                int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    const float s = sc[i];
-    const float q = quotient_for_e4m3(__uint_as_float((uint32_t)x[i] << 16), s, 1.0f / s);
-    out[i] = (uint8_t)pack_e4m3x4(q, 0.0f, 0.0f, 0.0f);
+    const u32x4 v = {(uint32_t)x[i], 0u, 0u, 0u};  // the value in the low half of the first dword
+    out[i] = (uint8_t)quantize8(v, sc[i]).x;
   }
 }
 

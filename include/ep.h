@@ -325,9 +325,9 @@ int ep_last_hip_error(void);
  *   ep_check_quant_e4m3: out[i] = the E4M3 code FP8 dispatch stores for the
  *                      BF16 value x[i] (bit pattern) under block scale s[i]:
  *                      the code of the correctly rounded quotient x / s,
- *                      through the dispatch kernels' own quotient routine;
- *                      defined for |x| <= 448 * s (every value a block with
- *                      that scale holds)
+ *                      through the dispatch kernels' own quantiser; defined
+ *                      for |x| <= 448 * s (every value a block with that
+ *                      scale holds)
  * in is a device fp32 array of n elements (x: n BF16 bit patterns and s: n
  * fp32 scales), out a device array of n codes (uint8) or BF16 bit patterns
  * (uint16); n >= 0.

@@ -389,8 +389,8 @@ def test_e4m3_conversion_exhaustive():
 
 def test_fp8_quantiser_exhaustive():
     """Every pair (block amax, BF16 x) with 0 < amax finite and |x| <= amax, both signs of x
-    (~1.07e9 pairs): the dispatch kernels' quotient routine (a multiplication by 1/s, with
-    the division taken near E4M3 rounding thresholds) gives the oracle's code of x / s."""
+    (~1.07e9 pairs): the dispatch kernels' quantiser (device division and E4M3 convert)
+    gives the oracle's code of x / s under that amax's block scale."""
     amax = np.arange(1, 0x7F80, dtype=np.int64)          # positive finite BF16 magnitudes
     s_of = (np.maximum(wl.bf16_bits_to_f32(amax.astype(np.uint16)), np.float32(1e-4)) /
             np.float32(448.0)).astype(np.float32)        # block scale per amax (fp32, as the oracle)

@@ -192,15 +192,16 @@ __global__ __launch_bounds__(64 * WPB) void dispatch_mx_kernel(RowParams p, int 
     }
     if (lane < 4 * sl.nc) {
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(sdst + (int64_t)s * nb, (uint32_t)nb);
+      // through the caches, as the FP8 scales (partial lines of neighbouring rows merge there)
       if (scol + 4u <= (uint32_t)nb) {
-        __builtin_amdgcn_raw_buffer_store_b32(my_sdw, rs, (int)scol, 0, AUX_ST);
+        __builtin_amdgcn_raw_buffer_store_b32(my_sdw, rs, (int)scol, 0, kAuxDefault);
       } else {
         // the row's last scales when H / 32 is not a multiple of 4: a dword
         // reaching past the row would be dropped whole by the range check,
         // so store byte by byte (bytes past the row are dropped)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(my_sdw >> (8 * b)), rs, (int)scol + b, 0, AUX_ST);
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(my_sdw >> (8 * b)), rs, (int)scol + b, 0, kAuxDefault);
       }
     }
   }
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(64 * WPB) void dispatch_prequantized_kernel(RowPara
 #pragma unroll
     for (int m = 0; m < (NC > 8 ? 2 : 1); ++m) {
       const int i = 64 * m + lane;
-      if (i < nsc) __builtin_amdgcn_raw_buffer_store_b32(scale[m], rs, (sc0 + i) * 4, 0, AUX_ST);
+      if (i < nsc) __builtin_amdgcn_raw_buffer_store_b32(scale[m], rs, (sc0 + i) * 4, 0, kAuxDefault);
     }
   }
   }

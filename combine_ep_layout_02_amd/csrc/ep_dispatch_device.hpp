@@ -159,9 +159,13 @@ static __device__ __forceinline__ void store_fp8_row(const RowParams& p, const S
     for (int m = 0; m < NC / 2; ++m)
       if (2 * m < sl.nc) store16<AUX_ST>(rd, ocol + 1024u * m, out[m]);
     if (lane < 4 * sl.nc) {
+      // The scales of consecutive receive rows are neighbours in recv_scale
+      // but come from different tokens: stored through the caches, the
+      // partial lines merge before they reach HBM (streamed as the rows are,
+      // they cost 10 us of the 113 us dispatch at 8192 tokens).
       const __amdgpu_buffer_rsrc_t rs =
           make_rsrc(static_cast<float*>(p.recv_scale) + (int64_t)s * nb, (uint32_t)nb * 4u);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(my_scale), rs, (int)scol, 0, AUX_ST);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(my_scale), rs, (int)scol, 0, kAuxDefault);
     }
   }
 }

@@ -63,14 +63,15 @@ __device__ __forceinline__ void widen8(u32x4 v, float* f) {
   f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
 }
 
-// K > 0: exactly K pairs per token, one batch.  K == 0: any k, in batches
-// of 8 pairs (g is re-read per batch, from L2).  g is loaded with the default
-// policy so that it stays cached for the grad_y scatter that follows; the
-// rows of y are streamed (AUX_Y).
+// The gate-weight gradients of token t.  K > 0: exactly K pairs per token,
+// one batch.  K == 0: any k, in batches of 8 pairs (g is re-read per batch,
+// from L2).  g is loaded with the default policy so that it stays cached for
+// the grad_y scatter that follows; the rows of y are streamed (AUX_Y).
+// Ends with a barrier after which `part` may be reused.
 template <int K, int AUX_Y>
-__global__ __launch_bounds__(64 * kMaxWaves) void grad_weights_kernel(BackParams p, int chunks) {
+__device__ __forceinline__ void grad_weights_token(const BackParams& p, int chunks, int t,
+                                                   float (&part)[kMaxWaves][kMaxTopk]) {
   constexpr int NB = K > 0 ? K : 8;
-  __shared__ float part[kMaxWaves][kMaxTopk];
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int waves = uniform(blockDim.x >> 6);
@@ -78,8 +79,6 @@ __global__ __launch_bounds__(64 * kMaxWaves) void grad_weights_kernel(BackParams
   const int k = K > 0 ? K : p.k;
   const uint32_t row_bytes = (uint32_t)H * 2u;
 
-  // one token per workgroup; a launch limited to a CU budget loops over tokens
-  for (int t = blockIdx.x; t < p.T; t += gridDim.x) {
   const int sl = lane < k ? p.slot[(int64_t)t * k + lane] : -1;
   const uint16_t* y = static_cast<const uint16_t*>(p.y);
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(static_cast<const uint16_t*>(p.g) + (int64_t)t * H, row_bytes);
@@ -128,17 +127,43 @@ __global__ __launch_bounds__(64 * kMaxWaves) void grad_weights_kernel(BackParams
     for (int w = 1; w < waves; ++w) acc += part[w][j];
     p.grad_w[(int64_t)t * k + j] = acc;
   }
-  __syncthreads();  // part is rewritten by the next token
+}
+
+// Whole-GPU launch: one workgroup per token.  (A token loop in this kernel
+// costs 20% here: 150 -> 182 us at 8192 tokens.)
+template <int K, int AUX_Y>
+__global__ __launch_bounds__(64 * kMaxWaves) void grad_weights_kernel(BackParams p, int chunks) {
+  __shared__ float part[kMaxWaves][kMaxTopk];
+  grad_weights_token<K, AUX_Y>(p, chunks, blockIdx.x, part);
+}
+
+// Launch limited to a CU budget: gridDim.x persistent workgroups loop over
+// the tokens.
+template <int K, int AUX_Y>
+__global__ __launch_bounds__(64 * kMaxWaves) void grad_weights_budget_kernel(BackParams p, int chunks) {
+  __shared__ float part[kMaxWaves][kMaxTopk];
+  for (int t = blockIdx.x; t < p.T; t += gridDim.x) {
+    grad_weights_token<K, AUX_Y>(p, chunks, t, part);
+    __syncthreads();  // part is rewritten by the next token
   }
+}
+
+template <int K, int AUX_Y>
+void launch_gw_aux(const BackParams& p, int waves, int chunks, hipStream_t stream) {
+  const dim3 block(64 * waves);
+  if (p.num_cus > 0)
+    hipLaunchKernelGGL((grad_weights_budget_kernel<K, AUX_Y>), dim3(p.num_cus < p.T ? p.num_cus : p.T), block, 0,
+                       stream, p, chunks);
+  else
+    hipLaunchKernelGGL((grad_weights_kernel<K, AUX_Y>), dim3(p.T), block, 0, stream, p, chunks);
 }
 
 template <int K>
 hipError_t launch_gw(const BackParams& p, int waves, int chunks, hipStream_t stream) {
-  const dim3 grid(p.num_cus > 0 && p.num_cus < p.T ? p.num_cus : p.T), block(64 * waves);
   if ((int64_t)p.T * p.k * p.H * 2 < kStreamingBytes)
-    hipLaunchKernelGGL((grad_weights_kernel<K, kAuxDefault>), grid, block, 0, stream, p, chunks);
+    launch_gw_aux<K, kAuxDefault>(p, waves, chunks, stream);
   else
-    hipLaunchKernelGGL((grad_weights_kernel<K, kAuxNT>), grid, block, 0, stream, p, chunks);
+    launch_gw_aux<K, kAuxNT>(p, waves, chunks, stream);
   return hipGetLastError();
 }
 

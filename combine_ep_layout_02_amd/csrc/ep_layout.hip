@@ -108,10 +108,11 @@ __global__ __launch_bounds__(64 * W) void layout_tiles_kernel(LayoutParams p) {
   const int64_t g0 = (int64_t)tile * p.TT * p.k;
   const int np = max(0, min(p.TT, p.T - tile * p.TT)) * p.k;
   int e, local;
+  tile_pass<W>(p, L, tile, &s_bad, e, local);
+
   if (single) {
     // Block 0 writes outputs and slots; all blocks share the padding rows.
     const bool lead = blockIdx.x == 0;
-    single_tile_pass<W>(p, L, lead, &s_bad, e, local);
     if (lead && tid == 0 && p.diag) { p.diag[0] = s_bad; p.diag[1] = 0; }
     scan_offsets(L.cnt_s, L.offs, p.E, p.A, p.C, s_part);  // barrier: diag[1] is zero before the adds
     if (lead) {
@@ -129,8 +130,6 @@ __global__ __launch_bounds__(64 * W) void layout_tiles_kernel(LayoutParams p) {
                       (int64_t)blockIdx.x * nthr + tid, (int64_t)gridDim.x * nthr);
     return;
   }
-
-  tile_pass<W>(p, L, tile, &s_bad, e, local);
 
   for (int ee = tid; ee < p.E; ee += nthr) p.ws_tile[(size_t)tile * p.E + ee] = L.cnt_s[ee];
   for (int r = tid; r < p.R; r += nthr) p.ws_rank[(size_t)tile * p.R + r] = L.rank_hist[r];

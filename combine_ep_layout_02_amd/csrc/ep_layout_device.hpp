@@ -217,98 +217,5 @@ static __device__ void tile_pass(const LayoutParams& p, const TileLds<W>& L, int
   local_out = e >= 0 ? L.pref[w * E + e] + (int)__popcll(L.masks[w * E + e] & ((1ull << lane) - 1ull)) : -1;
 }
 
-// Counts and stable ranks of a batch that is a single tile (at most 64*W
-// pairs; pair p is thread p), built for latency.  Each wavefront finds, with
-// one ballot per bit of the expert id, the mask of its lanes that hold the
-// same expert as each lane: the pair's rank inside its window is the number
-// of those lanes below it, and the lowest lane of each group stores the
-// group's size into a [W][E] count table (in the masks' space).  A pair's
-// rank is its in-window rank plus its expert's counts in the earlier
-// windows; an expert's total is its column sum.  Same results as tile_pass
-// for tile 0.  want_ranks: also the distinct tokens per rank and the invalid
-// ids (only the workgroup that writes the outputs needs them).  Ends with a
-// barrier.
-template <int W>
-static __device__ void single_tile_pass(const LayoutParams& p, const TileLds<W>& L, bool want_ranks, int* s_bad,
-                                        int& e_out, int& local_out) {
-  const int E = p.E, R = p.R, k = p.k;
-  const int tid = threadIdx.x, nthr = 64 * W;
-  const int np = p.T * k;
-  int* cnt_w = reinterpret_cast<int*>(L.masks);
-  const bool small_r = R <= 64;
-
-  const int v = tid < np ? p.idx[tid] : -1;
-  for (int i = tid; i < W * E; i += nthr) cnt_w[i] = 0;
-  if (want_ranks) {
-    L.tokrank[tid] = 0;
-    for (int i = tid; i < E; i += nthr) L.rank_of[i] = udiv((uint32_t)i, p.magic_per);
-    for (int i = tid; i < R; i += nthr) L.rank_hist[i] = 0;
-    if (tid == 0) *s_bad = 0;
-  }
-  int e = -1;
-  bool bad = false;
-  if (tid < np) {
-    if (v >= 0 && v < E) e = v;
-    else bad = (v != -1);
-  }
-  L.idx_s[tid] = e;
-  const int w = tid >> 6, lane = tid & 63;
-  const uint64_t below = (1ull << lane) - 1ull;
-  uint64_t same = __ballot(e >= 0);  // invalid lanes never join a group
-  for (int b = 0; (1 << b) < E; ++b) {
-    const bool bit = (e >> b) & 1;
-    const uint64_t with = __ballot(bit);
-    same &= bit ? with : ~with;
-  }
-  const int rank_in = (int)__popcll(same & below);
-  __syncthreads();  // count table zeroed, rank_of filled
-
-  if (e >= 0 && (same & below) == 0) cnt_w[w * E + e] = (int)__popcll(same);
-  if (want_ranks) {
-    if (e >= 0 && small_r)
-      atomicOr(reinterpret_cast<unsigned long long*>(&L.tokrank[udiv((uint32_t)tid, p.magic_k)]),
-               1ull << L.rank_of[e]);
-    const uint64_t bb = __ballot(bad);
-    if (lane == 0 && bb) atomicAdd(s_bad, (int)__popcll(bb));
-  }
-  __syncthreads();
-
-  int local = -1;
-  if (e >= 0) {
-    local = rank_in;
-    for (int w2 = 0; w2 < w; ++w2) local += cnt_w[w2 * E + e];
-  }
-  for (int ee = tid; ee < E; ee += nthr) {
-    int c = 0;
-#pragma unroll
-    for (int w2 = 0; w2 < W; ++w2) c += cnt_w[w2 * E + ee];
-    L.cnt_s[ee] = c;
-  }
-  if (want_ranks) {
-    const int nt = p.T;
-    if (small_r) {
-      if (tid < nt) {
-        uint64_t m = L.tokrank[tid];
-        while (m) {
-          atomicAdd(&L.rank_hist[__builtin_ctzll(m)], 1);
-          m &= m - 1;
-        }
-      }
-    } else if (e >= 0) {
-      const int r = L.rank_of[e];
-      const int tl = udiv((uint32_t)tid, p.magic_k);
-      bool first = true;
-      for (int q = tl * k; q < tid; ++q) {
-        const int e2 = L.idx_s[q];
-        if (e2 >= 0 && L.rank_of[e2] == r) { first = false; break; }
-      }
-      if (first) atomicAdd(&L.rank_hist[r], 1);
-    }
-  }
-  __syncthreads();
-  e_out = e;
-  local_out = local;
-}
-
 }  // namespace lay
 }  // namespace ep

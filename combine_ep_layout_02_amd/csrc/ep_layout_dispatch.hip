@@ -10,9 +10,8 @@
 // separate layout launch and reading the slots back from memory:
 //   1. each wavefront issues the loads of its token slice (x does not depend
 //      on the layout), so they are in flight during steps 2-3;
-//   2. the workgroup's 1024 threads run the single-tile pass and the offset
-//      scan of ep_layout (ep_layout_device.hpp) and keep every pair's slot
-//      in LDS;
+//   2. the workgroup's 1024 threads run the tile pass and the offset scan of
+//      ep_layout (ep_layout_device.hpp) and keep every pair's slot in LDS;
 //   3. workgroup 0 writes the layout outputs exactly as ep_layout does, and
 //      all workgroups share the src_pair padding rows;
 //   4. each wavefront writes its slice's copies (BF16 or FP8) to the slots
@@ -61,8 +60,8 @@ __global__ __launch_bounds__(64 * kW) void layout_dispatch_kernel(LayoutParams l
 
   // 2. the tile's layout in LDS (one pair per thread)
   int e, local;
+  tile_pass<kW>(lp, L, 0, &s_bad, e, local);
   const bool lead = blockIdx.x == 0;
-  single_tile_pass<kW>(lp, L, lead, &s_bad, e, local);
   if (lead && tid == 0 && lp.diag) { lp.diag[0] = s_bad; lp.diag[1] = 0; }
   scan_offsets(L.cnt_s, L.offs, lp.E, lp.A, lp.C, s_part);  // barrier: diag[1] is zero before the adds
   const int np = lp.T * lp.k;

@@ -203,7 +203,7 @@ EP_EXPORT ep_status_t ep_layout_dispatch(const ep_shape_t* shape, const int32_t*
   st2 = dispatch_args(shape, x, slot, recv_dtype, recv_x, recv_scale, rp);
   if (st2 != EP_OK) return st2;
   if (shape->num_tokens > 0 && shape->num_cus == 0 && (recv_dtype == EP_BF16 || recv_dtype == EP_FP8_E4M3) &&
-      ep::layout_dispatch_fusable(pl))
+      ep::layout_dispatch_fusable(pl, lp))
     return hip_status(ep::launch_layout_dispatch(pl, lp, rp, recv_dtype == EP_FP8_E4M3, stream));
   const hipError_t err = ep::launch_layout(pl, lp, stream);
   if (err != hipSuccess) return hip_status(err);

@@ -88,9 +88,9 @@ hipError_t launch_dispatch_bf16(const RowParams& p, hipStream_t stream);  // wei
 hipError_t launch_dispatch_fp8(const RowParams& p, hipStream_t stream);
 hipError_t launch_dispatch_mx(const RowParams& p, int elem_bits, hipStream_t stream);  // 8: MXFP8, 4: MXFP4
 hipError_t launch_dispatch_prequantized(const RowParams& p, hipStream_t stream);     // src = E4M3 codes
-// Layout and BF16 / FP8 dispatch in one launch when the batch is one layout
-// tile of 16 windows (see ep_layout_dispatch.hip).
-bool layout_dispatch_fusable(const LayoutPlan& plan);
+// Layout and BF16 / FP8 dispatch in one launch for batches of at most 1024
+// pairs (see ep_layout_dispatch.hip).
+bool layout_dispatch_fusable(const LayoutPlan& plan, const LayoutParams& lp);
 hipError_t launch_layout_dispatch(const LayoutPlan& plan, LayoutParams lp, const RowParams& rp, bool fp8,
                                   hipStream_t stream);
 hipError_t launch_combine(const RowParams& p, hipStream_t stream);  // weights null: unit weights

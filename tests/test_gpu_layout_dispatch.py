@@ -16,7 +16,10 @@ pytestmark = pytest.mark.gpu
 
 
 def run_fused(shape, idx, x_bits, dtype):
+    """ep_layout_dispatch into fresh buffers, every output pre-filled with a marker."""
     bufs = ep.LayoutBuffers.allocate(shape, DEV)
+    for t in (bufs.expert_count, bufs.expert_offset, bufs.rank_count, bufs.rank_offset, bufs.slot, bufs.diag):
+        t.fill_(-9)
     bufs.src_pair.fill_(-7)      # every row must be written (pair id or -1)
     rx, rs = ep.alloc_recv(shape, dtype, DEV)
     rx.view(torch.uint8).fill_(0x5A)
@@ -30,6 +33,10 @@ def run_fused(shape, idx, x_bits, dtype):
 def check(shape, w_rows, idx, x, dtype, lay):
     bufs, rx, rs = run_fused(shape, idx, x, dtype)
     assert_layout_equal(bufs, lay)
+    check_recv(w_rows, x, dtype, lay, rx, rs)
+
+
+def check_recv(w_rows, x, dtype, lay, rx, rs):
     held = lay.src_pair >= 0
     got = rx.view(torch.uint8).cpu().numpy().reshape(w_rows, -1)
     if dtype == ep.EP_BF16:
@@ -80,6 +87,121 @@ def test_layout_dispatch_edge_cases(case, dtype):
     check(shape_of(w), w.recv_rows, idx, x, dtype, lay)
 
 
+# Shapes around the two fused forms: the direct form (expert_alignment 1 or a
+# padded layout, at most 1024 pairs) and the tile form (expert_alignment > 1).
+FUSED_FORMS = [
+    # name, T, H, k, E, R, A, C, ids: "perm" (distinct per token) or "any" (repeats, -1 and invalid ids)
+    ("e2048_rank_per_expert", 8, 512, 8, 2048, 2048, 1, 0, "perm"),
+    ("e2048_padded", 64, 512, 8, 2048, 64, 1, 4, "any"),
+    ("k64_1024_pairs", 16, 1024, 64, 128, 8, 1, 0, "any"),
+    ("repeated_experts_flat", 128, 512, 8, 16, 4, 1, 0, "any"),
+    ("repeated_experts_padded", 128, 512, 8, 16, 4, 1, 24, "any"),
+    ("padded_one_expert", 50, 256, 1, 1, 1, 1, 20, "perm"),
+    ("ragged_39_pairs_flat", 13, 256, 3, 16, 4, 1, 0, "any"),
+    ("ragged_39_pairs_padded", 13, 256, 3, 16, 4, 1, 3, "any"),
+    ("ragged_1023_pairs_padded", 341, 128, 3, 64, 8, 1, 16, "any"),
+    ("flat_one_expert", 1000, 256, 1, 1, 1, 1, 0, "any"),
+    ("padded_capacity_2", 128, 7168, 8, 256, 8, 1, 2, "any"),
+    ("tile_form_aligned4", 100, 512, 4, 16, 4, 4, 0, "any"),
+    ("tile_form_aligned16_decode", 128, 7168, 8, 256, 8, 16, 0, "perm"),
+    ("two_calls_1025_pairs", 205, 256, 5, 32, 4, 1, 0, "any"),
+]
+
+
+def form_ids(rng, T, k, E, kind):
+    if kind == "perm":
+        return _idx(rng, T, k, E)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    u = rng.random(idx.shape)
+    idx[u < 0.1] = -1
+    idx[(u >= 0.1) & (u < 0.13)] = E + 3
+    idx[(u >= 0.13) & (u < 0.15)] = -4
+    return idx
+
+
+@pytest.mark.parametrize("dtype", [ep.EP_FP8_E4M3, ep.EP_BF16])
+@pytest.mark.parametrize("case", FUSED_FORMS, ids=lambda c: c[0])
+def test_layout_dispatch_forms(case, dtype):
+    name, T, H, k, E, R, A, C, kind = case
+    log(f"[layout-dispatch-form] {name} dtype={dtype}")
+    w = wl.custom(name, T, H, E, R, k, seed=97, capacity=C, expert_alignment=A)
+    rng = np.random.default_rng(97)
+    idx = form_ids(rng, T, k, E, kind)
+    lay = oracle.layout(idx, E, R, A, C)
+    x = wl.normal_bf16(97, 0, T, H)
+    check(shape_of(w), w.recv_rows, idx, x, dtype, lay)
+
+
+@pytest.mark.parametrize("C", [0, 24], ids=["flat", "padded"])
+def test_layout_dispatch_without_src_pair_and_diag(C):
+    """The optional outputs may be null; the others and the receive rows are unchanged."""
+    T, H, k, E, R = 128, 512, 8, 16, 4
+    log(f"[layout-dispatch-null] C={C}")
+    w = wl.custom("null_outputs", T, H, E, R, k, seed=96, capacity=C)
+    shape = shape_of(w)
+    idx = form_ids(np.random.default_rng(96), T, k, E, "any")
+    lay = oracle.layout(idx, E, R, 1, C)
+    x = wl.normal_bf16(96, 0, T, H)
+    b = ep.LayoutBuffers.allocate(shape, DEV)
+    rx, rs = ep.alloc_recv(shape, ep.EP_FP8_E4M3, DEV)
+    rx.view(torch.uint8).fill_(0x5A)
+    ep.ep_layout_dispatch(shape, dev_i32(idx), b.expert_count, b.expert_offset, b.rank_count, b.rank_offset, b.slot,
+                          None, None, b.workspace, dev_bf16(x), ep.EP_FP8_E4M3, rx, rs)
+    torch.cuda.synchronize()
+    assert np.array_equal(b.expert_count.cpu().numpy(), lay.expert_count)
+    assert np.array_equal(b.expert_offset.cpu().numpy(), lay.expert_offset)
+    assert np.array_equal(b.rank_count.cpu().numpy(), lay.rank_count)
+    assert np.array_equal(b.rank_offset.cpu().numpy(), lay.rank_offset)
+    assert np.array_equal(b.slot.cpu().numpy().reshape(lay.slot.shape), lay.slot)
+    check_recv(w.recv_rows, x, ep.EP_FP8_E4M3, lay, rx, rs)
+
+
 def test_layout_dispatch_under_budget_takes_two_calls():
     w, inp, lay = inputs("decode")
     check(dataclasses.replace(shape_of(w), num_cus=4), w.recv_rows, inp.topk_idx, inp.x, ep.EP_FP8_E4M3, lay)
+
+
+def test_decode_step_replays_from_a_hip_graph():
+    """The decode step (fused layout + FP8 dispatch, then combine) captured in a HIP graph: every replay, with
+    eager calls between replays, gives the eager results (no call records a memset or allocates)."""
+    w, inp, lay_ref = inputs("decode", with_y=True)
+    log("[graph] decode step")
+    shape = shape_of(w)
+    lay = ep.LayoutBuffers.allocate(shape, DEV)
+    x = dev_bf16(inp.x)
+    y = dev_bf16(inp.y)
+    wts = torch.from_numpy(inp.topk_weights).to(DEV)
+    out = torch.empty_like(x)
+    rq, rs = ep.alloc_recv(shape, ep.EP_FP8_E4M3, DEV)
+    idx = dev_i32(inp.topk_idx)
+
+    def step():
+        lay.run_dispatch(idx, x, ep.EP_FP8_E4M3, rq, rs)
+        ep.ep_combine(shape, y, lay.slot, wts, out)
+
+    side = torch.cuda.Stream(DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream(DEV).wait_stream(side)
+    torch.cuda.synchronize()
+    held = lay_ref.src_pair >= 0
+    want_q, want_s = oracle.dispatch_fp8(inp.x, lay_ref.slot, w.recv_rows)
+    want_out = oracle.combine(inp.y, lay_ref.slot, inp.topk_weights)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (lay.slot, lay.src_pair, lay.expert_count, lay.diag):
+            t.fill_(-9)
+        rq.view(torch.uint8).fill_(0x11)
+        out.view(torch.int16).fill_(0x1111)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_layout_equal(lay, lay_ref)
+        assert np.array_equal(rq.cpu().numpy()[held], want_q[held]), f"replay {rep}: FP8 codes"
+        assert np.array_equal(rs.cpu().numpy()[held], want_s[held]), f"replay {rep}: scales"
+        assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), want_out), f"replay {rep}: combine"
+        step()  # eager work between replays
+        torch.cuda.synchronize()

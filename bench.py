@@ -133,7 +133,7 @@ class Step:
         self.dispatch = ep.prepare_dispatch(self.shape, self.x, self.lay.slot, self.dtype, self.recv_x,
                                             self.recv_scale, stream)
         self.combine = ep.prepare_combine(self.shape, self.y, self.lay.slot, self.wts, self.out, stream)
-        # layout and dispatch as one call (one launch when the batch is one layout tile)
+        # layout and dispatch as one call (one launch for batches of at most 1024 pairs)
         self.layout_dispatch = self.lay.prepare_dispatch(self.idx, self.x, self.dtype, self.recv_x, self.recv_scale,
                                                          stream)
 
@@ -600,7 +600,7 @@ def main():
                "dispatch_us": round(float(np.median(d_stage[:, 1])) * 1e3, 2),
                "combine_us": round(float(np.median(d_stage[:, 2])) * 1e3, 2),
                "bytes": dstep.bytes,
-               "note": "one call = layout + FP8 dispatch (ep_layout_dispatch: one launch for this one-tile batch) "
+               "note": "one call = layout + FP8 dispatch (ep_layout_dispatch: one launch for this 1024-pair batch) "
                        "+ combine of 128 tokens into the padded [256, 128, 7168] layout; mean over 500 back-to-back "
                        "calls (inputs stay in the 256 MB Infinity Cache); us_per_call_separate_layout runs "
                        "ep_layout and ep_dispatch as two launches; stage times are medians with events around "

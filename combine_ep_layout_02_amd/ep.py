@@ -213,7 +213,7 @@ def _layout_args(shape: EpShape, topk_idx, expert_count, expert_offset, rank_cou
 
 def ep_layout_dispatch(shape: EpShape, topk_idx, expert_count, expert_offset, rank_count, rank_offset, slot,
                        src_pair, diag, workspace, x, recv_dtype: int, recv_x, recv_scale=None, stream=None) -> None:
-    """ep_layout then ep_dispatch; one launch for single-tile batches (the decode shape)."""
+    """ep_layout then ep_dispatch; one launch for batches of at most 1024 pairs (the decode shape)."""
     largs = _layout_args(shape, topk_idx, expert_count, expert_offset, rank_count, rank_offset, slot, src_pair,
                          diag, workspace)
     dargs = _dispatch_args(shape, x, slot, recv_dtype, recv_x, recv_scale)
@@ -469,7 +469,7 @@ class LayoutBuffers:
 
     def run_dispatch(self, topk_idx: torch.Tensor, x, recv_dtype: int, recv_x, recv_scale=None,
                      stream=None) -> "LayoutBuffers":
-        """Layout and dispatch in one call (one launch for single-tile batches)."""
+        """Layout and dispatch in one call (one launch for batches of at most 1024 pairs)."""
         ep_layout_dispatch(self.shape, topk_idx, self.expert_count, self.expert_offset, self.rank_count,
                            self.rank_offset, self.slot, self.src_pair, self.diag, self.workspace, x, recv_dtype,
                            recv_x, recv_scale, stream)

@@ -206,14 +206,15 @@ ep_status_t ep_dispatch(const ep_shape_t *shape, const void *x, const int32_t *s
 
 /*
  * ep_layout followed by ep_dispatch, with the same arguments and bit for bit
- * the same results.  When the batch fits one layout tile (T * k <= 1024
- * pairs with E <= 256; the decode shape) and recv_dtype is EP_BF16 or
- * EP_FP8_E4M3 and num_cus is 0, it is one launch: every workgroup of the
- * dispatch rebuilds the (small) layout in LDS while its token loads are in
- * flight, instead of waiting for a layout launch and reading the slots back
- * (the per-step layout of the decode path: [DOC] item 3; [GN] "Patrones de
- * uso en entrenamiento, prefill y decoding").  Otherwise it enqueues the
- * two calls.  Argument checks are those of the two calls.
+ * the same results.  It is one launch when recv_dtype is EP_BF16 or
+ * EP_FP8_E4M3, num_cus is 0 and the batch holds at most 1024 pairs
+ * (T * k <= 1024; the decode shape) with either a padded layout (capacity
+ * > 0, E <= 2048) or expert_alignment 1 (E <= 1024), or fits one layout tile
+ * (E <= 256): the dispatch works the slots out itself instead of waiting for
+ * a layout launch and reading them back (the per-step layout of the decode
+ * path: [DOC] item 3; [GN] "Patrones de uso en entrenamiento, prefill y
+ * decoding").  Otherwise it enqueues the two calls.  Argument checks are
+ * those of the two calls.
  */
 ep_status_t ep_layout_dispatch(const ep_shape_t *shape, const int32_t *topk_idx,
                                int32_t *expert_count, int32_t *expert_offset,

@@ -446,6 +446,49 @@ def calibration_copy(dev, reps=3):
     return 2 * (1 << 30) / (float(np.median(ms)) / 1e3) / 1e9
 
 
+def mix_ceilings(step, reps=10):
+    """The streaming probe (ep_probe_stream: contiguous 1 KiB chunks, no gathers)
+    at each stage's own read:write byte mix, on the step's own buffers, under
+    each of its four cache policies; the best is the practical ceiling of a
+    plain copy with that mix on this machine.  Overwrites the step's outputs;
+    run after the timed legs."""
+    res = {}
+    policies = ("nt/nt", "default/default", "nt/sc1", "default/nt")
+    # combine reads 8 bytes per byte written (y rows -> out); FP8 dispatch writes ~4 per byte read (x -> recv_x)
+    for name, src, dst, r, wr in (("combine", step.y, step.out, 16, 2), ("dispatch", step.x, step.recv_x, 2, 8)):
+        units = min(src.numel() * src.element_size() // (r * 1024), dst.numel() * dst.element_size() // (wr * 1024))
+        nbytes = units * (r + wr) * 1024
+        per = {}
+        for pol, pname in enumerate(policies):
+            ms = []
+            for _ in range(reps + 2):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                ep.ep_probe_stream(src, dst, units, r, wr, pol)
+                e1.record()
+                torch.cuda.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            per[pname] = round(nbytes / (float(np.median(ms[2:])) / 1e3) / 1e9, 1)
+        best = max(per, key=per.get)
+        res[name] = {"read_KiB_per_unit": r, "write_KiB_per_unit": wr, "units": units, "bytes": nbytes,
+                     "GBps": per[best], "policy": best, "GBps_by_policy": per}
+    return res
+
+
+def host_cpu():
+    """Model name and usable cores of the host that runs the CPU oracle."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "usable_cores": len(os.sched_getaffinity(0)), "logical_cpus": os.cpu_count()}
+
+
 def traffic_from(fetch_dir, write_dir):
     """Combine-kernel HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
     each scaled by what the same counter reads for the 1 GiB calibration copy."""
@@ -618,6 +661,8 @@ def main():
             torch.cuda.empty_cache()
     del flush
 
+    log("[bench] mix ceilings")
+    mix = mix_ceilings(step)
     copy_gbps = calibration_copy(dev, reps=3 if args.calibration_copy else 5)
     cb = cbp = None
     if not args.no_cpu_baseline:
@@ -661,7 +706,15 @@ def main():
                          "the L2s hold any of the step's data"},
         "roofline": {"kernel": "combine", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": comb_bytes},
+                     "algorithmic_bytes_per_launch": comb_bytes,
+                     "mix_ceiling_GBps": mix["combine"]["GBps"],
+                     "frac_of_mix_ceiling": round(achieved / mix["combine"]["GBps"], 4)},
+        "mix_ceilings": dict(mix, note="ep_probe_stream at each stage's read:write mix (contiguous 1 KiB chunks, no "
+                                       "gathers) on the step's buffers, best of four cache policies; *_frac = the "
+                                       "stage's GB/s over it",
+                             combine_frac=round(achieved / mix["combine"]["GBps"], 4),
+                             dispatch_frac=round(bytes_dispatch(w, True) / (disp_ms / 1e3) / 1e9
+                                                 / mix["dispatch"]["GBps"], 4)),
         "copy_ceiling": {"GBps": round(copy_gbps, 1), "kernel": "torch bitwise_not, 1 GiB in + 1 GiB out",
                          "step_frac_of_copy": round(value / copy_gbps, 4)},
         "decode": dec,
@@ -670,6 +723,7 @@ def main():
         "configs": configs,
         "cpu_baseline": cb,
         "cpu_baseline_all_cores": cbp,
+        "host_cpu": host_cpu() if cb is not None else None,
         "wall_s_timed": round(wall, 4),
     }
     print(json.dumps(result), flush=True)

@@ -6,7 +6,7 @@ seeded synthetic inputs; `build` compiles the library in-tree."""
 from .ep import (EP_BF16, EP_FP8_E4M3, EP_MXFP4_E2M1, EP_MXFP8_E4M3, EpError, EpShape, LayoutBuffers, Prepared, alloc_recv, ep_abi_version,
                  ep_check_cvt_bf16, ep_check_cvt_e2m1, ep_check_cvt_e4m3, ep_combine, ep_combine_backward,
                  ep_dispatch, ep_dispatch_backward, ep_dispatch_prequantized, prepare_dispatch_prequantized,
-                 recv_layout, ep_layout_dispatch, prepare_layout_dispatch, ep_check_quant_e4m3, ep_layout, ep_layout_workspace_bytes, ep_recv_rows, ep_status_string, lib,
+                 recv_layout, ep_layout_dispatch, prepare_layout_dispatch, ep_check_quant_e4m3, ep_probe_stream, ep_layout, ep_layout_workspace_bytes, ep_recv_rows, ep_status_string, lib,
                  library_path, prepare_combine, prepare_combine_backward, prepare_dispatch,
                  prepare_dispatch_backward, prepare_layout)
 
@@ -14,6 +14,6 @@ __all__ = ["EP_BF16", "EP_FP8_E4M3", "EP_MXFP8_E4M3", "EP_MXFP4_E2M1", "EpError"
            "ep_abi_version", "prepare_layout", "prepare_dispatch", "prepare_combine",
            "prepare_dispatch_backward", "prepare_combine_backward", "ep_dispatch_backward", "ep_combine_backward",
            "ep_dispatch_prequantized", "prepare_dispatch_prequantized", "ep_check_cvt_e2m1", "recv_layout",
-           "ep_layout_dispatch", "prepare_layout_dispatch", "ep_check_quant_e4m3",
+           "ep_layout_dispatch", "prepare_layout_dispatch", "ep_check_quant_e4m3", "ep_probe_stream",
            "ep_check_cvt_bf16", "ep_check_cvt_e4m3", "ep_combine", "ep_dispatch", "ep_layout",
            "ep_layout_workspace_bytes", "ep_recv_rows", "ep_status_string", "lib", "library_path"]

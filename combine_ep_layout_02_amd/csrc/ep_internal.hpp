@@ -100,5 +100,7 @@ hipError_t launch_check_cvt_e4m3(const float* in, uint8_t* out, int64_t n, hipSt
 hipError_t launch_check_cvt_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream);
 hipError_t launch_check_cvt_e2m1(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 hipError_t launch_check_quant_e4m3(const uint16_t* x, const float* s, uint8_t* out, int64_t n, hipStream_t stream);
+hipError_t launch_probe_stream(const void* src, void* dst, int64_t units, int read_chunks, int write_chunks,
+                               int policy, hipStream_t stream);
 
 }  // namespace ep

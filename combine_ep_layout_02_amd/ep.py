@@ -33,7 +33,7 @@ EXPORTED = ("ep_recv_rows", "ep_layout_workspace_bytes", "ep_layout", "ep_dispat
             "ep_dispatch_prequantized",
             "ep_combine", "ep_dispatch_backward", "ep_combine_backward", "ep_status_string", "ep_abi_version",
             "ep_last_hip_error", "ep_check_cvt_e4m3", "ep_check_cvt_bf16", "ep_check_cvt_e2m1",
-            "ep_check_quant_e4m3")
+            "ep_check_quant_e4m3", "ep_probe_stream")
 
 
 class EpError(RuntimeError):
@@ -127,6 +127,8 @@ def lib() -> ctypes.CDLL:
         L.ep_check_cvt_e2m1.argtypes = [vp, vp, ctypes.c_int64, vp]
         L.ep_check_cvt_bf16.restype = st
         L.ep_check_cvt_bf16.argtypes = [vp, vp, ctypes.c_int64, vp]
+        L.ep_probe_stream.restype = st
+        L.ep_probe_stream.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
         _lib = L
     return _lib
 
@@ -343,6 +345,18 @@ def ep_check_quant_e4m3(x, s, out, stream=None) -> None:
     _check("ep_check_quant_e4m3", lib().ep_check_quant_e4m3(
         _ptr(x, "x", _BF16_LIKE, n, optional=n == 0), _ptr(s, "s", torch.float32, n, optional=n == 0),
         _ptr(out, "out", _BYTE_LIKE, n, optional=n == 0), n, _stream(stream)))
+
+
+def ep_probe_stream(src, dst, units: int, read_chunks: int, write_chunks: int, policy: int = 0,
+                    stream=None) -> None:
+    """Measurement helper: streams units * read_chunks KiB of src into units * write_chunks KiB of dst
+    (policy 0..3 picks the loads' and stores' cache policy)."""
+    for t, name, kib in ((src, "src", read_chunks), (dst, "dst", write_chunks)):
+        if t.numel() * t.element_size() < units * kib * 1024:
+            raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {units * kib * 1024}")
+    _check("ep_probe_stream", lib().ep_probe_stream(_ptr(src, "src", optional=units == 0),
+                                                    _ptr(dst, "dst", optional=units == 0), units, read_chunks,
+                                                    write_chunks, policy, _stream(stream)))
 
 
 def ep_check_cvt_e2m1(inp, out, stream=None) -> None:

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 5
+#define EP_ABI_VERSION 6
 
 /* Limits checked by every entry point (EP_ERR_UNSUPPORTED beyond them). */
 #define EP_MAX_EXPERTS 2048
@@ -338,6 +338,22 @@ ep_status_t ep_check_cvt_bf16(const float *in, uint16_t *out, int64_t n, hipStre
 ep_status_t ep_check_cvt_e2m1(const float *in, uint8_t *out, int64_t n, hipStream_t stream);
 ep_status_t ep_check_quant_e4m3(const uint16_t *x, const float *s, uint8_t *out, int64_t n,
                                 hipStream_t stream);
+
+/*
+ * Streaming probe, for measurement only (not part of the method): the
+ * practical memory ceiling of a read:write mix.  Unit u of `units` reads
+ * read_chunks contiguous 1 KiB chunks of src at byte offset
+ * u * read_chunks * 1024, XORs them (16-byte lanes), and writes the result
+ * to write_chunks contiguous 1 KiB chunks of dst at byte offset
+ * u * write_chunks * 1024.  Cache policy: 0 non-temporal loads and
+ * stores, 1 default loads and stores, 2 non-temporal loads and device-scope
+ * (sc1) stores, 3 default loads and non-temporal stores.  src must hold
+ * units * read_chunks KiB and dst units * write_chunks KiB, both device
+ * memory, 16-byte aligned.  read_chunks is 1, 2, 4, 8 or 16; write_chunks
+ * is 1..64; policy 0..3; units >= 0.
+ */
+ep_status_t ep_probe_stream(const void *src, void *dst, int64_t units, int read_chunks,
+                            int write_chunks, int policy, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_abi_version_and_status_strings(L):
     header = open(HEADER).read()
-    assert ep.ep_abi_version() == int(re.search(r"#define EP_ABI_VERSION (\d+)", header).group(1)) == 5
+    assert ep.ep_abi_version() == int(re.search(r"#define EP_ABI_VERSION (\d+)", header).group(1)) == 6
     for code in range(6):
         s = ep.ep_status_string(code)
         assert s.startswith("EP_"), s
@@ -271,6 +271,16 @@ def test_check_helpers_argument_checks(L):
     assert L.ep_check_quant_e4m3(FAKE + 1, FAKE, FAKE, 4, None) == MISALIGNED
     assert L.ep_check_quant_e4m3(FAKE, FAKE + 2, FAKE, 4, None) == MISALIGNED
     assert L.ep_check_quant_e4m3(None, None, None, 0, None) == OK
+    assert L.ep_probe_stream(FAKE, FAKE, -1, 1, 1, 0, None) == INVALID
+    assert L.ep_probe_stream(FAKE, FAKE, 4, 3, 1, 0, None) == INVALID
+    assert L.ep_probe_stream(FAKE, FAKE, 4, 1, 0, 0, None) == INVALID
+    assert L.ep_probe_stream(FAKE, FAKE, 4, 1, 65, 0, None) == INVALID
+    assert L.ep_probe_stream(FAKE, FAKE, 4, 1, 1, 4, None) == INVALID
+    assert L.ep_probe_stream(FAKE, FAKE, 4, 1, 1, -1, None) == INVALID
+    assert L.ep_probe_stream(None, FAKE, 4, 1, 1, 0, None) == INVALID
+    assert L.ep_probe_stream(FAKE + 8, FAKE, 4, 1, 1, 0, None) == MISALIGNED
+    assert L.ep_probe_stream(FAKE, FAKE + 4, 4, 1, 1, 0, None) == MISALIGNED
+    assert L.ep_probe_stream(None, None, 0, 16, 64, 3, None) == OK
 
 
 def test_binding_rejects_host_tensors():

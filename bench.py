@@ -394,13 +394,16 @@ def summarize_config(w, fp8, dev, steps, flush):
     """Warm (back-to-back) and cold (flushed) step time of one more workload."""
     step = Step(w, dev, fp8=fp8)
     total_ms, _ = time_steps(step, steps, 5)
+    fused_ms, _ = time_steps(step, steps, 5, fused=True)
     cold = time_cold(step, 10, flush)
     nbytes = step.bytes
     warm_us = total_ms / steps * 1e3
+    fused_us = fused_ms / steps * 1e3
     cold_us = float(np.median(cold)) * 1e3
     return {"dispatch": "fp8_e4m3" if fp8 else "bf16", "tokens": w.num_tokens, "hidden": w.hidden,
             "experts": w.num_experts, "topk": w.num_topk, "capacity": w.capacity, "bytes_per_step": nbytes,
             "warm_us": round(warm_us, 2), "warm_GBps": round(nbytes / warm_us / 1e3, 1),
+            "warm_us_layout_dispatch_call": round(fused_us, 2),
             "cold_us": round(cold_us, 2), "cold_GBps": round(nbytes / cold_us / 1e3, 1)}
 
 

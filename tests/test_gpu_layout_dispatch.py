@@ -1,4 +1,4 @@
-"""GPU parity of ep_layout_dispatch (layout fused into dispatch for single-tile batches, the
+"""GPU parity of ep_layout_dispatch (layout fused into dispatch for batches of at most 1024 pairs, the
 two calls otherwise) against the CPU oracle: every layout output and every receive byte."""
 import dataclasses
 
@@ -55,7 +55,7 @@ def check_recv(w_rows, x, dtype, lay, rx, rs):
                                         ("tiny", ep.EP_FP8_E4M3), ("decode", ep.EP_MXFP4_E2M1),
                                         ("mid", ep.EP_BF16), ("v3", ep.EP_FP8_E4M3)])
 def test_layout_dispatch_matches_oracle(name, dtype):
-    """Single-tile workloads take the fused kernel (BF16 / FP8); MX, mid and v3 take the two calls."""
+    """Batches of at most 1024 pairs take the fused kernel (BF16 / FP8); MX, mid and v3 take the two calls."""
     w, inp, lay = inputs(name)
     log(f"[layout-dispatch] {name} dtype={dtype}")
     check(shape_of(w), w.recv_rows, inp.topk_idx, inp.x, dtype, lay)

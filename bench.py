@@ -16,9 +16,10 @@ reading a 1 GiB buffer, so no cache holds its data), the decode-shaped
 workload's microseconds per call, the backward pair's kernel times on the
 same handle, dispatch in every receive format (BF16, FP8, MXFP8, MXFP4,
 pre-quantised FP8), warm and cold step times of the tiny, mid
-and 16K-token skewed workloads, a plain 1 GiB copy as the practical
-bandwidth ceiling, and the CPU oracle timed on this host (one thread) on the
-same workload.
+and 16K-token skewed workloads, a plain 1 GiB copy and a streaming probe
+at each stage's own read:write mix as practical bandwidth ceilings, and the
+CPU oracle timed on this host (one thread, and all usable cores, with the
+CPU model) on the same workload.
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 
@@ -574,8 +575,8 @@ def cpu_baseline_parallel(step, threads):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="v3", choices=["v3", "skew"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")

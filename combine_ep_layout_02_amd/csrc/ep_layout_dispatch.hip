@@ -14,13 +14,14 @@
 // expert e,
 //   flat:   slot = #{valid pairs with id < e} + #{pairs before (t, j) with id e}
 //   padded: pos  = #{pairs before (t, j) with id e},  slot = e*C + pos if pos < C
-// ("before" in (token, k-index) order: the stable counting sort).  Every
-// wavefront loads the batch's ids (16 per lane) and counts with ballots, so
-// no workgroup builds a layout and no wavefront waits for another:
+// ("before" in (token, k-index) order: the stable counting sort).  Each
+// workgroup of 4 wavefronts stages the batch's ids in LDS once (16 per lane
+// of each wavefront); after that no wavefront waits for another:
 //   * dispatch wavefronts (one per token slice) issue the loads of their row,
-//     count their token's k slots (k ballot sweeps over the ids), write the
-//     token's slot / src_pair entries (first slice only) and store the row's
-//     copies with the dispatch kernels' row code (ep_dispatch_device.hpp);
+//     count their token's k slots with a small LDS histogram of their own
+//     (atomic adds, order independent), write the token's slot / src_pair
+//     entries (first slice only) and store the row's copies with the
+//     dispatch kernels' row code (ep_dispatch_device.hpp);
 //   * job wavefronts after them take the other outputs, each a count over
 //     the ids: one job per expert (its count, offset, the rank offset it
 //     starts, its padding rows), one per rank (distinct tokens, through a

@@ -104,7 +104,11 @@ FUSED_FORMS = [
     ("padded_capacity_2", 128, 7168, 8, 256, 8, 1, 2, "any"),
     ("tile_form_aligned4", 100, 512, 4, 16, 4, 4, 0, "any"),
     ("tile_form_aligned16_decode", 128, 7168, 8, 256, 8, 16, 0, "perm"),
+    ("h256_one_slice_per_token", 170, 256, 6, 64, 8, 1, 0, "any"),
     ("two_calls_1025_pairs", 205, 256, 5, 32, 4, 1, 0, "any"),
+    ("two_calls_decode_512_tokens_padded", 512, 7168, 8, 256, 8, 1, 128, "perm"),
+    ("two_calls_padded_4096_pairs_drops", 1024, 512, 4, 64, 8, 1, 48, "any"),
+    ("two_calls_e2048_flat_2048_pairs", 256, 512, 8, 2048, 64, 1, 0, "any"),
 ]
 
 

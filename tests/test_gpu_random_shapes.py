@@ -5,8 +5,12 @@ The fixed edge cases elsewhere pin one corner each; here 200 seeded draws mix th
 with repeated experts, masked and invalid ids, flat layouts with alignment 1 to 16 and padded layouts whose
 capacity may drop pairs.  Each draw runs ep_layout, ep_layout_dispatch, BF16 / FP8 / MXFP8 / MXFP4 dispatch,
 combine and the backward pair through the C ABI and compares every output with the oracle (bit for bit;
-grad_weights within its stated bound).  Inputs come from the seeded generators only.
+grad_weights within its stated bound); every fourth draw repeats dispatch, combine and the backward pair
+under a CU budget (persistent workgroups), which must give the same bytes.  Inputs come from the seeded
+generators only.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -128,3 +132,21 @@ def test_random_shape(seed):
     assert np.array_equal(got_gy[held], want_gy[held]) and (got_gy[~held] == SENTINEL).all()
     err = np.abs(gw.cpu().numpy().astype(np.float64) - want_gw)
     assert (err <= gw_bound(x, y, lay.slot, H)).all()
+
+    if seed % 4 == 1:
+        # the same calls under a CU budget: persistent workgroups looping over the work, same bytes
+        budget = dataclasses.replace(shape, num_cus=int(np.random.default_rng([seed, 778]).choice([1, 3, 17, 100])))
+        log(f"  budget {budget.num_cus}")
+        bq, bs = ep.alloc_recv(shape, ep.EP_FP8_E4M3, DEV)
+        ep.ep_dispatch(budget, dev_bf16(x), slot, ep.EP_FP8_E4M3, bq, bs)
+        bout = torch.full((T, H), SENTINEL, dtype=torch.int16, device=DEV)
+        ep.ep_combine(budget, dev_bf16(y), slot, dev_f32(d["weights"]), bout)
+        bgx = torch.full((T, H), SENTINEL, dtype=torch.int16, device=DEV)
+        ep.ep_dispatch_backward(budget, dev_bf16(y), slot, bgx)
+        bgy = torch.full((rows, H), SENTINEL, dtype=torch.int16, device=DEV)
+        bgw = torch.full((T, k), float("nan"), dtype=torch.float32, device=DEV)
+        ep.ep_combine_backward(budget, dev_bf16(x), dev_bf16(y), slot, dev_f32(d["weights"]), bgy, bgw)
+        torch.cuda.synchronize()
+        assert np.array_equal(bq.view(torch.uint8).cpu().numpy()[held], wq[held])
+        assert np.array_equal(bs.cpu().numpy()[held], ws[held])
+        assert torch.equal(bout, out) and torch.equal(bgx, gx) and torch.equal(bgy, gy) and torch.equal(bgw, gw)

@@ -3,11 +3,11 @@
 The fixed edge cases elsewhere pin one corner each; here 200 seeded draws mix them: token counts from 0 to
 500, hidden sizes of 128 to 2048 columns, 1 to 2048 experts in any dividing number of ranks, top-k up to 12
 with repeated experts, masked and invalid ids, flat layouts with alignment 1 to 16 and padded layouts whose
-capacity may drop pairs.  Each draw runs ep_layout, ep_layout_dispatch, BF16 / FP8 / MXFP8 / MXFP4 dispatch,
-combine and the backward pair through the C ABI and compares every output with the oracle (bit for bit;
-grad_weights within its stated bound); every fourth draw repeats dispatch, combine and the backward pair
-under a CU budget (persistent workgroups), which must give the same bytes.  Inputs come from the seeded
-generators only.
+capacity may drop pairs.  Each draw runs ep_layout, ep_layout_dispatch, BF16 / FP8 / MXFP8 / MXFP4 and
+pre-quantised dispatch, combine and the backward pair through the C ABI and compares every output with the
+oracle (bit for bit; grad_weights within its stated bound); every fourth draw repeats dispatch, combine
+and the backward pair under a CU budget (persistent workgroups), which must give the same bytes.  Inputs
+come from the seeded generators only.
 """
 import dataclasses
 
@@ -111,6 +111,18 @@ def test_random_shape(seed):
         want_q, want_s = oracle.dispatch_mx(x, lay.slot, rows, bits)
         assert np.array_equal(mq.view(torch.uint8).cpu().numpy()[held], want_q[held]), f"MX{bits} codes"
         assert np.array_equal(ms.view(torch.uint8).cpu().numpy()[held], want_s[held]), f"MX{bits} scales"
+
+    # caller-quantised codes and scales, passed through
+    prng = np.random.default_rng([seed, 779])
+    xq = prng.integers(0, 256, (T, H), dtype=np.uint8)
+    xs = prng.standard_normal((T, H // 128)).astype(np.float32)
+    pq = torch.full((rows, H), 0x5A, dtype=torch.uint8, device=DEV)
+    ps = torch.full((rows, H // 128), -1.0, dtype=torch.float32, device=DEV)
+    ep.ep_dispatch_prequantized(shape, torch.from_numpy(xq).to(DEV), dev_f32(xs), slot, pq, ps)
+    torch.cuda.synchronize()
+    want_pq, want_ps = oracle.dispatch_prequantized(xq, xs, lay.slot, rows)
+    assert np.array_equal(pq.cpu().numpy()[held], want_pq[held]) and np.array_equal(ps.cpu().numpy()[held], want_ps[held])
+    assert (pq.cpu().numpy()[~held] == 0x5A).all()
 
     # combine (the fixed FMA chain: bit for bit)
     out = torch.full((T, H), SENTINEL, dtype=torch.int16, device=DEV)

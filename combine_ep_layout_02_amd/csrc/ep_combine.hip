@@ -123,7 +123,7 @@ template <int K, int WPB, int NG>
 void launch_kw(const RowParams& p, int blocks, int chunks, hipStream_t stream) {
   const dim3 block(64 * WPB);
   if ((int64_t)p.T * p.k * p.H * 2 < kStreamingBytes)
-    hipLaunchKernelGGL((combine_kernel<K, kAuxDefault, kAuxDefault, WPB, NG>), dim3(blocks), block, 0, stream, p,
+    hipLaunchKernelGGL((combine_kernel<K, kAuxDefault, kAuxSmallStore, WPB, NG>), dim3(blocks), block, 0, stream, p,
                        chunks);
   else if ((int64_t)p.T * p.H * 2 <= kCacheableOutputBytes)
     hipLaunchKernelGGL((combine_kernel<K, kAuxNT, kAuxSC1, WPB, NG>), dim3(blocks), block, 0, stream, p, chunks);

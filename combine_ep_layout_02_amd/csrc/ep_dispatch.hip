@@ -309,7 +309,7 @@ void launch_bf16_ncsw(const DispatchSplit& s, const RowParams& p, bool streaming
     hipLaunchKernelGGL((dispatch_bf16_kernel<NC, kAuxDefault, kAuxNT, SCALED, WPB>), dim3(s.blocks), dim3(64 * WPB),
                        0, stream, p, s.wpt, s.cpw, s.nchunks);
   else
-    hipLaunchKernelGGL((dispatch_bf16_kernel<NC, kAuxDefault, kAuxDefault, SCALED, WPB>), dim3(s.blocks),
+    hipLaunchKernelGGL((dispatch_bf16_kernel<NC, kAuxDefault, kAuxSmallStore, SCALED, WPB>), dim3(s.blocks),
                        dim3(64 * WPB), 0, stream, p, s.wpt, s.cpw, s.nchunks);
 }
 
@@ -335,7 +335,7 @@ void launch_fp8_ncw(const DispatchSplit& s, const RowParams& p, bool streaming, 
     hipLaunchKernelGGL((dispatch_fp8_kernel<NC, kAuxDefault, kAuxNT, WPB>), dim3(s.blocks), dim3(64 * WPB), 0, stream,
                        p, s.wpt, s.cpw, s.nchunks);
   else
-    hipLaunchKernelGGL((dispatch_fp8_kernel<NC, kAuxDefault, kAuxDefault, WPB>), dim3(s.blocks), dim3(64 * WPB), 0,
+    hipLaunchKernelGGL((dispatch_fp8_kernel<NC, kAuxDefault, kAuxSmallStore, WPB>), dim3(s.blocks), dim3(64 * WPB), 0,
                        stream, p, s.wpt, s.cpw, s.nchunks);
 }
 
@@ -345,7 +345,7 @@ void launch_mx_ncw(const DispatchSplit& s, const RowParams& p, bool streaming, h
     hipLaunchKernelGGL((dispatch_mx_kernel<NC, kAuxDefault, kAuxNT, WPB, ELEM>), dim3(s.blocks), dim3(64 * WPB), 0,
                        stream, p, s.wpt, s.cpw, s.nchunks);
   else
-    hipLaunchKernelGGL((dispatch_mx_kernel<NC, kAuxDefault, kAuxDefault, WPB, ELEM>), dim3(s.blocks),
+    hipLaunchKernelGGL((dispatch_mx_kernel<NC, kAuxDefault, kAuxSmallStore, WPB, ELEM>), dim3(s.blocks),
                        dim3(64 * WPB), 0, stream, p, s.wpt, s.cpw, s.nchunks);
 }
 
@@ -373,7 +373,7 @@ void launch_pq_ncw(const DispatchSplit& s, const RowParams& p, bool streaming, h
     hipLaunchKernelGGL((dispatch_prequantized_kernel<NC, kAuxDefault, kAuxNT, WPB>), dim3(s.blocks), dim3(64 * WPB),
                        0, stream, p, s.wpt, s.cpw, s.nchunks);
   else
-    hipLaunchKernelGGL((dispatch_prequantized_kernel<NC, kAuxDefault, kAuxDefault, WPB>), dim3(s.blocks),
+    hipLaunchKernelGGL((dispatch_prequantized_kernel<NC, kAuxDefault, kAuxSmallStore, WPB>), dim3(s.blocks),
                        dim3(64 * WPB), 0, stream, p, s.wpt, s.cpw, s.nchunks);
 }
 

@@ -331,9 +331,9 @@ __global__ __launch_bounds__(64 * kDirectWaves) void layout_dispatch_direct_kern
     if (slots >= 0 && lp.src_pair) lp.src_pair[slots] = tk + lane;
   }
   if constexpr (FP8)
-    store_fp8_row<NC, kAuxDefault>(rp, sl, lane, v, slots);
+    store_fp8_row<NC, kAuxSmallStore>(rp, sl, lane, v, slots);
   else
-    store_bf16_row<NC, kAuxDefault, false>(rp, sl, lane, v, slots);
+    store_bf16_row<NC, kAuxSmallStore, false>(rp, sl, lane, v, slots);
 }
 
 template <int NC, bool FP8, bool PADDED>
@@ -417,9 +417,9 @@ __global__ __launch_bounds__(64 * kW) void layout_dispatch_kernel(LayoutParams l
   if (has) {
     const int slots = lane < rp.k ? slot_s[sl.t * rp.k + lane] : -1;
     if constexpr (FP8)
-      store_fp8_row<NC, kAuxDefault>(rp, sl, lane, v, slots);
+      store_fp8_row<NC, kAuxSmallStore>(rp, sl, lane, v, slots);
     else
-      store_bf16_row<NC, kAuxDefault, false>(rp, sl, lane, v, slots);
+      store_bf16_row<NC, kAuxSmallStore, false>(rp, sl, lane, v, slots);
   }
 }
 

@@ -109,6 +109,13 @@ FUSED_FORMS = [
     ("two_calls_decode_512_tokens_padded", 512, 7168, 8, 256, 8, 1, 128, "perm"),
     ("two_calls_padded_4096_pairs_drops", 1024, 512, 4, 64, 8, 1, 48, "any"),
     ("two_calls_e2048_flat_2048_pairs", 256, 512, 8, 2048, 64, 1, 0, "any"),
+    ("two_calls_e2048_64_pair_tiles", 1024, 128, 4, 2048, 16, 1, 0, "any"),
+    ("two_calls_e2048_padded", 600, 128, 8, 2048, 64, 1, 2, "any"),
+    ("two_calls_aligned4_masked", 3000, 256, 4, 64, 8, 4, 0, "any"),
+    ("two_calls_aligned16", 2048, 384, 8, 256, 8, 16, 0, "perm"),
+    ("two_calls_rank_per_2_experts", 1500, 256, 4, 256, 128, 1, 0, "any"),
+    ("two_calls_ragged_last_tile", 1000, 384, 6, 48, 6, 1, 0, "any"),
+    ("two_calls_128_tiles", 16384, 128, 8, 256, 8, 1, 0, "perm"),
 ]
 
 
@@ -192,6 +199,82 @@ def test_decode_step_replays_from_a_hip_graph():
     held = lay_ref.src_pair >= 0
     want_q, want_s = oracle.dispatch_fp8(inp.x, lay_ref.slot, w.recv_rows)
     want_out = oracle.combine(inp.y, lay_ref.slot, inp.topk_weights)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (lay.slot, lay.src_pair, lay.expert_count, lay.diag):
+            t.fill_(-9)
+        rq.view(torch.uint8).fill_(0x11)
+        out.view(torch.int16).fill_(0x1111)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_layout_equal(lay, lay_ref)
+        assert np.array_equal(rq.cpu().numpy()[held], want_q[held]), f"replay {rep}: FP8 codes"
+        assert np.array_equal(rs.cpu().numpy()[held], want_s[held]), f"replay {rep}: scales"
+        assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), want_out), f"replay {rep}: combine"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_calls_in_a_row_share_one_workspace():
+    """Several ep_layout_dispatch calls over many layout tiles on one workspace, with ep_layout calls between
+    them, each with other ids: every call is exact (the workspace needs no initial contents)."""
+    T, H, k, E, R = 2000, 256, 8, 64, 8
+    w = wl.custom("workspace_reuse", T, H, E, R, k, seed=95)
+    shape = shape_of(w)
+    b = ep.LayoutBuffers.allocate(shape, DEV)
+    b.workspace.fill_(0x7B)
+    rx, rs = ep.alloc_recv(shape, ep.EP_FP8_E4M3, DEV)
+    x = wl.normal_bf16(95, 0, T, H)
+    for call in range(4):
+        log(f"[layout-dispatch-reuse] call {call}")
+        idx = form_ids(np.random.default_rng([95, call]), T, k, E, "any")
+        lay = oracle.layout(idx, E, R, 1, 0)
+        b.src_pair.fill_(-7)
+        rx.view(torch.uint8).fill_(0x5A)
+        b.run_dispatch(dev_i32(idx), dev_bf16(x), ep.EP_FP8_E4M3, rx, rs)
+        torch.cuda.synchronize()
+        assert_layout_equal(b, lay)
+        check_recv(w.recv_rows, x, ep.EP_FP8_E4M3, lay, rx, rs)
+        rev = idx[::-1].copy()
+        b.run(dev_i32(rev))  # ep_layout on the same workspace
+        torch.cuda.synchronize()
+        assert_layout_equal(b, oracle.layout(rev, E, R, 1, 0))
+
+
+def test_multi_tile_step_replays_from_a_hip_graph():
+    """Layout over 16 tiles + FP8 dispatch, then combine, captured in a HIP graph: every replay, with eager
+    calls between replays, is exact."""
+    T, H, k, E, R = 2048, 1024, 8, 256, 8
+    log("[graph] multi-tile step")
+    w = wl.custom("graph_tiles", T, H, E, R, k, seed=94)
+    shape = shape_of(w)
+    idx_h = form_ids(np.random.default_rng(94), T, k, E, "perm")
+    lay_ref = oracle.layout(idx_h, E, R, 1, 0)
+    x_h = wl.normal_bf16(94, 0, T, H)
+    y_h = wl.normal_bf16(94, 2, w.recv_rows, H)
+    wts_h = np.random.default_rng([94, 1]).standard_normal((T, k)).astype(np.float32)
+    lay = ep.LayoutBuffers.allocate(shape, DEV)
+    x, y, idx = dev_bf16(x_h), dev_bf16(y_h), dev_i32(idx_h)
+    wts = torch.from_numpy(wts_h).to(DEV)
+    out = torch.empty_like(x)
+    rq, rs = ep.alloc_recv(shape, ep.EP_FP8_E4M3, DEV)
+
+    def step():
+        lay.run_dispatch(idx, x, ep.EP_FP8_E4M3, rq, rs)
+        ep.ep_combine(shape, y, lay.slot, wts, out)
+
+    side = torch.cuda.Stream(DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream(DEV).wait_stream(side)
+    torch.cuda.synchronize()
+    held = lay_ref.src_pair >= 0
+    want_q, want_s = oracle.dispatch_fp8(x_h, lay_ref.slot, w.recv_rows)
+    want_out = oracle.combine(y_h, lay_ref.slot, wts_h)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()

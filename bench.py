@@ -453,11 +453,12 @@ def calibration_copy(dev, reps=3):
 def mix_ceilings(step, reps=10):
     """The streaming probe (ep_probe_stream: contiguous 1 KiB chunks, no gathers)
     at each stage's own read:write byte mix, on the step's own buffers, under
-    each of its four cache policies; the best is the practical ceiling of a
-    plain copy with that mix on this machine.  Overwrites the step's outputs;
-    run after the timed legs."""
+    each of its four cache policies, in round-robin and in XCD-contiguous unit
+    order; the best is the practical ceiling of a plain copy with that mix on
+    this machine.  Overwrites the step's outputs; run after the timed legs."""
     res = {}
     policies = ("nt/nt", "default/default", "nt/sc1", "default/nt")
+    policies = policies + tuple(p + " xcd" for p in policies)  # + 4: units in XCD-contiguous order
     # combine reads 8 bytes per byte written (y rows -> out); FP8 dispatch writes ~4 per byte read (x -> recv_x)
     for name, src, dst, r, wr in (("combine", step.y, step.out, 16, 2), ("dispatch", step.x, step.recv_x, 2, 8)):
         units = min(src.numel() * src.element_size() // (r * 1024), dst.numel() * dst.element_size() // (wr * 1024))
@@ -714,7 +715,7 @@ def main():
                      "mix_ceiling_GBps": mix["combine"]["GBps"],
                      "frac_of_mix_ceiling": round(achieved / mix["combine"]["GBps"], 4)},
         "mix_ceilings": dict(mix, note="ep_probe_stream at each stage's read:write mix (contiguous 1 KiB chunks, no "
-                                       "gathers) on the step's buffers, best of four cache policies; *_frac = the "
+                                       "gathers) on the step's buffers, best of four cache policies x two unit orders; *_frac = the "
                                        "stage's GB/s over it",
                              combine_frac=round(achieved / mix["combine"]["GBps"], 4),
                              dispatch_frac=round(bytes_dispatch(w, True) / (disp_ms / 1e3) / 1e9

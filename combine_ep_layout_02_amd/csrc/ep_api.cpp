@@ -330,7 +330,7 @@ EP_EXPORT ep_status_t ep_check_quant_e4m3(const uint16_t* x, const float* s, uin
 
 EP_EXPORT ep_status_t ep_probe_stream(const void* src, void* dst, int64_t units, int read_chunks, int write_chunks,
                                       int policy, hipStream_t stream) {
-  if (units < 0 || write_chunks < 1 || write_chunks > 64 || policy < 0 || policy > 3) return EP_ERR_INVALID_ARG;
+  if (units < 0 || write_chunks < 1 || write_chunks > 64 || policy < 0 || policy > 7) return EP_ERR_INVALID_ARG;
   if (read_chunks != 1 && read_chunks != 2 && read_chunks != 4 && read_chunks != 8 && read_chunks != 16)
     return EP_ERR_INVALID_ARG;
   if (units > 0 && (!src || !dst)) return EP_ERR_INVALID_ARG;

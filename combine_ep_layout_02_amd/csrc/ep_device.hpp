@@ -46,6 +46,15 @@ constexpr int kAuxSC1 = 16;  // sc1: device-scope store
 //     (a 235 MB output thrashes the cache and sc1 loses 5% at 16384 tokens).
 constexpr int64_t kStreamingBytes = (int64_t)64 << 20;
 constexpr int kAuxSmallStore = kAuxSC1;
+
+// Workgroups are dealt to the chip's 8 XCDs round robin (workgroup b to XCD
+// b mod 8).  This renumbering, a bijection on [0, nb), gives XCD x one
+// contiguous eighth of the logical workgroups [x*q + min(x, r), ...) with
+// q = nb / 8, r = nb % 8, instead of every eighth one.
+__device__ __forceinline__ int xcd_contiguous(int b, int nb) {
+  const int q = nb >> 3, r = nb & 7, x = b & 7;
+  return x * q + (x < r ? x : r) + (b >> 3);
+}
 constexpr int64_t kCacheableOutputBytes = (int64_t)128 << 20;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {

@@ -42,18 +42,30 @@ constexpr int kMaxChunks = 16;     // most 512-column chunks a wavefront holds (
 constexpr int kWavesPerBlock = 4;  // 256 threads (whole-GPU launches)
 
 // Slices are handed out grid-stride: a whole-GPU launch has one wavefront per
-// slice and runs the loop once; a launch limited to a CU budget runs that
-// many persistent workgroups, each wavefront taking every (grid * WPB)-th
-// slice.
-#define EP_FOR_EACH_SLICE(WPB, total, wave)                                                       \
-  for (int wave = uniform((int)blockIdx.x * (WPB) + (int)(threadIdx.x >> 6)); wave < (total); \
+// slice and runs the loop once; a launch limited to a CU budget runs that many
+// persistent workgroups, each wavefront taking every (grid * WPB)-th
+// slice.  The loop starts at workgroup index `blk` (the hardware index, or
+// its XCD-contiguous renumbering below).
+#define EP_FOR_EACH_SLICE(WPB, total, wave, blk)                                     \
+  for (int wave = uniform((blk) * (WPB) + (int)(threadIdx.x >> 6)); wave < (total); \
        wave += (int)gridDim.x * (WPB))
+
+// xcd_contiguous (ep_device.hpp) gives XCD x one contiguous eighth of the
+// slices instead of every eighth workgroup.  Measured at 8192 tokens x 7168, whole-GPU launches: FP8 93.2-93.7 vs
+// 100.3-100.7 us, MXFP8 92.6 vs 100.4, MXFP4 55.7 vs 57.6, and FP8 at 4096 x
+// 4096 x top-6 23.5 vs 24.1; runs of 16 to 256 workgroups per XCD instead of
+// one eighth gain little or nothing.  It is applied to the formats with
+// block scales: BF16 dispatch (188.0 vs 188.4 us; 42.4 vs 41.5 at 4096 x
+// 4096), combine (187.9 vs 175.3) and decode-sized launches do not gain.
+__device__ __forceinline__ int first_block(int xcd) {
+  return xcd ? xcd_contiguous((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x;
+}
 
 // NC: chunk capacity of the instantiation (>= chunks per wavefront).
 template <int NC, int AUX_LD, int AUX_ST, bool SCALED, int WPB>
 __global__ __launch_bounds__(64 * WPB) void dispatch_bf16_kernel(RowParams p, int wpt, int cpw, int nchunks) {
   const int lane = threadIdx.x & 63;
-  EP_FOR_EACH_SLICE(WPB, p.T * wpt, wave) {
+  EP_FOR_EACH_SLICE(WPB, p.T * wpt, wave, (int)blockIdx.x) {
     const Slice sl = slice_of(wave, wpt, cpw, nchunks);
     u32x4 v[NC];
     load_row<NC, AUX_LD>(p, sl, lane, v);
@@ -62,9 +74,10 @@ __global__ __launch_bounds__(64 * WPB) void dispatch_bf16_kernel(RowParams p, in
 }
 
 template <int NC, int AUX_LD, int AUX_ST, int WPB>
-__global__ __launch_bounds__(64 * WPB) void dispatch_fp8_kernel(RowParams p, int wpt, int cpw, int nchunks) {
+__global__ __launch_bounds__(64 * WPB) void dispatch_fp8_kernel(RowParams p, int wpt, int cpw, int nchunks,
+                                                                int xcd) {
   const int lane = threadIdx.x & 63;
-  EP_FOR_EACH_SLICE(WPB, p.T * wpt, wave) {
+  EP_FOR_EACH_SLICE(WPB, p.T * wpt, wave, first_block(xcd)) {
     const Slice sl = slice_of(wave, wpt, cpw, nchunks);
     u32x4 v[NC];
     load_row<NC, AUX_LD>(p, sl, lane, v);
@@ -125,10 +138,11 @@ struct MxFormat<4> {
 // lane L < 4 * nc holds dword L % 4 of chunk L / 4, so one store per receive
 // row writes the slice's scales as one contiguous run.
 template <int NC, int AUX_LD, int AUX_ST, int WPB, int ELEM>
-__global__ __launch_bounds__(64 * WPB) void dispatch_mx_kernel(RowParams p, int wpt, int cpw, int nchunks) {
+__global__ __launch_bounds__(64 * WPB) void dispatch_mx_kernel(RowParams p, int wpt, int cpw, int nchunks,
+                                                               int xcd) {
   using F = MxFormat<ELEM>;
   const int lane = threadIdx.x & 63;
-  EP_FOR_EACH_SLICE(WPB, p.T * wpt, wave) {
+  EP_FOR_EACH_SLICE(WPB, p.T * wpt, wave, first_block(xcd)) {
   const Slice sl = slice_of(wave, wpt, cpw, nchunks);
   u32x4 v[NC];
   load_row<NC, AUX_LD>(p, sl, lane, v);
@@ -220,9 +234,9 @@ __global__ __launch_bounds__(64 * WPB) void dispatch_mx_kernel(RowParams p, int 
 // ---------------------------------------------------------------------------
 template <int NC, int AUX_LD, int AUX_ST, int WPB>
 __global__ __launch_bounds__(64 * WPB) void dispatch_prequantized_kernel(RowParams p, int wpt, int cpw,
-                                                                         int nchunks) {
+                                                                         int nchunks, int xcd) {
   const int lane = threadIdx.x & 63;
-  EP_FOR_EACH_SLICE(WPB, p.T * wpt, wave) {
+  EP_FOR_EACH_SLICE(WPB, p.T * wpt, wave, first_block(xcd)) {
   const Slice sl = slice_of(wave, wpt, cpw, nchunks);
   u32x4 v[NC];
   load_row<NC, AUX_LD>(p, sl, lane, v);  // p.H counts two-byte columns
@@ -333,20 +347,20 @@ template <int NC, int WPB>
 void launch_fp8_ncw(const DispatchSplit& s, const RowParams& p, bool streaming, hipStream_t stream) {
   if (streaming)
     hipLaunchKernelGGL((dispatch_fp8_kernel<NC, kAuxDefault, kAuxNT, WPB>), dim3(s.blocks), dim3(64 * WPB), 0, stream,
-                       p, s.wpt, s.cpw, s.nchunks);
+                       p, s.wpt, s.cpw, s.nchunks, (int)!s.budget);
   else
     hipLaunchKernelGGL((dispatch_fp8_kernel<NC, kAuxDefault, kAuxSmallStore, WPB>), dim3(s.blocks), dim3(64 * WPB), 0,
-                       stream, p, s.wpt, s.cpw, s.nchunks);
+                       stream, p, s.wpt, s.cpw, s.nchunks, 0);
 }
 
 template <int NC, int WPB, int ELEM>
 void launch_mx_ncw(const DispatchSplit& s, const RowParams& p, bool streaming, hipStream_t stream) {
   if (streaming)
     hipLaunchKernelGGL((dispatch_mx_kernel<NC, kAuxDefault, kAuxNT, WPB, ELEM>), dim3(s.blocks), dim3(64 * WPB), 0,
-                       stream, p, s.wpt, s.cpw, s.nchunks);
+                       stream, p, s.wpt, s.cpw, s.nchunks, (int)!s.budget);
   else
     hipLaunchKernelGGL((dispatch_mx_kernel<NC, kAuxDefault, kAuxSmallStore, WPB, ELEM>), dim3(s.blocks),
-                       dim3(64 * WPB), 0, stream, p, s.wpt, s.cpw, s.nchunks);
+                       dim3(64 * WPB), 0, stream, p, s.wpt, s.cpw, s.nchunks, 0);
 }
 
 template <int NC, int ELEM>
@@ -371,10 +385,10 @@ template <int NC, int WPB>
 void launch_pq_ncw(const DispatchSplit& s, const RowParams& p, bool streaming, hipStream_t stream) {
   if (streaming)
     hipLaunchKernelGGL((dispatch_prequantized_kernel<NC, kAuxDefault, kAuxNT, WPB>), dim3(s.blocks), dim3(64 * WPB),
-                       0, stream, p, s.wpt, s.cpw, s.nchunks);
+                       0, stream, p, s.wpt, s.cpw, s.nchunks, (int)!s.budget);
   else
     hipLaunchKernelGGL((dispatch_prequantized_kernel<NC, kAuxDefault, kAuxSmallStore, WPB>), dim3(s.blocks),
-                       dim3(64 * WPB), 0, stream, p, s.wpt, s.cpw, s.nchunks);
+                       dim3(64 * WPB), 0, stream, p, s.wpt, s.cpw, s.nchunks, 0);
 }
 
 template <int NC>

@@ -9,7 +9,9 @@
 // byte mix allows on the same machine.  The cache policy is a parameter (policy 0: non-temporal loads and stores;
 // 1: default loads and stores; 2: non-temporal loads, device-scope sc1
 // stores; 3: default loads, non-temporal stores), so a caller can take the
-// best of them as the ceiling.
+// best of them as the ceiling.  Policy + 4: the same, with units taken in
+// XCD-contiguous order (each XCD one contiguous eighth of them), the order
+// the scaled dispatch kernels use.
 //
 // Unit u (one wavefront each, grid-stride over units): reads chunks
 // [u*r, (u+1)*r) of src, XORs them lane-wise into one 16-byte value per lane
@@ -26,9 +28,10 @@ constexpr int kProbeWaves = 4;         // wavefronts per workgroup
 
 template <int R, int AUX_LD, int AUX_ST>
 __global__ __launch_bounds__(64 * kProbeWaves) void probe_stream_kernel(const uint8_t* src, uint8_t* dst,
-                                                                         int64_t units, int w) {
+                                                                         int64_t units, int w, int xcd) {
   const int lane = threadIdx.x & 63;
-  for (int64_t u = (int64_t)blockIdx.x * kProbeWaves + (threadIdx.x >> 6); u < units;
+  const int blk = xcd ? xcd_contiguous((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x;
+  for (int64_t u = (int64_t)blk * kProbeWaves + (threadIdx.x >> 6); u < units;
        u += (int64_t)gridDim.x * kProbeWaves) {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + u * R * kChunk, (uint32_t)(R * kChunk));
     u32x4 v[R];
@@ -43,20 +46,21 @@ __global__ __launch_bounds__(64 * kProbeWaves) void probe_stream_kernel(const ui
 }
 
 template <int R, int AUX_LD, int AUX_ST>
-void launch_rp(const void* src, void* dst, int64_t units, int w, hipStream_t stream) {
+void launch_rp(const void* src, void* dst, int64_t units, int w, int xcd, hipStream_t stream) {
   const int64_t blocks = (units + kProbeWaves - 1) / kProbeWaves;
   const unsigned grid = (unsigned)(blocks < 65536 * 8 ? blocks : 65536 * 8);
   hipLaunchKernelGGL((probe_stream_kernel<R, AUX_LD, AUX_ST>), dim3(grid), dim3(64 * kProbeWaves), 0, stream,
-                     static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), units, w);
+                     static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), units, w, xcd);
 }
 
 template <int R>
 void launch_r(const void* src, void* dst, int64_t units, int w, int policy, hipStream_t stream) {
-  switch (policy) {
-    case 0: launch_rp<R, kAuxNT, kAuxNT>(src, dst, units, w, stream); break;
-    case 1: launch_rp<R, kAuxDefault, kAuxDefault>(src, dst, units, w, stream); break;
-    case 2: launch_rp<R, kAuxNT, kAuxSC1>(src, dst, units, w, stream); break;
-    default: launch_rp<R, kAuxDefault, kAuxNT>(src, dst, units, w, stream); break;
+  const int xcd = policy >> 2;
+  switch (policy & 3) {
+    case 0: launch_rp<R, kAuxNT, kAuxNT>(src, dst, units, w, xcd, stream); break;
+    case 1: launch_rp<R, kAuxDefault, kAuxDefault>(src, dst, units, w, xcd, stream); break;
+    case 2: launch_rp<R, kAuxNT, kAuxSC1>(src, dst, units, w, xcd, stream); break;
+    default: launch_rp<R, kAuxDefault, kAuxNT>(src, dst, units, w, xcd, stream); break;
   }
 }
 

@@ -350,7 +350,7 @@ def ep_check_quant_e4m3(x, s, out, stream=None) -> None:
 def ep_probe_stream(src, dst, units: int, read_chunks: int, write_chunks: int, policy: int = 0,
                     stream=None) -> None:
     """Measurement helper: streams units * read_chunks KiB of src into units * write_chunks KiB of dst
-    (policy 0..3 picks the loads' and stores' cache policy)."""
+    (policy 0..3 picks the loads' and stores' cache policy; + 4 takes the units in XCD-contiguous order)."""
     for t, name, kib in ((src, "src", read_chunks), (dst, "dst", write_chunks)):
         if t.numel() * t.element_size() < units * kib * 1024:
             raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {units * kib * 1024}")

@@ -347,10 +347,12 @@ ep_status_t ep_check_quant_e4m3(const uint16_t *x, const float *s, uint8_t *out,
  * to write_chunks contiguous 1 KiB chunks of dst at byte offset
  * u * write_chunks * 1024.  Cache policy: 0 non-temporal loads and
  * stores, 1 default loads and stores, 2 non-temporal loads and device-scope
- * (sc1) stores, 3 default loads and non-temporal stores.  src must hold
+ * (sc1) stores, 3 default loads and non-temporal stores; policy + 4 takes the
+ * units in XCD-contiguous order (each of the 8 XCDs one contiguous eighth)
+ * instead of round robin.  src must hold
  * units * read_chunks KiB and dst units * write_chunks KiB, both device
  * memory, 16-byte aligned.  read_chunks is 1, 2, 4, 8 or 16; write_chunks
- * is 1..64; policy 0..3; units >= 0.
+ * is 1..64; policy 0..7; units >= 0.
  */
 ep_status_t ep_probe_stream(const void *src, void *dst, int64_t units, int read_chunks,
                             int write_chunks, int policy, hipStream_t stream);

@@ -275,12 +275,12 @@ def test_check_helpers_argument_checks(L):
     assert L.ep_probe_stream(FAKE, FAKE, 4, 3, 1, 0, None) == INVALID
     assert L.ep_probe_stream(FAKE, FAKE, 4, 1, 0, 0, None) == INVALID
     assert L.ep_probe_stream(FAKE, FAKE, 4, 1, 65, 0, None) == INVALID
-    assert L.ep_probe_stream(FAKE, FAKE, 4, 1, 1, 4, None) == INVALID
+    assert L.ep_probe_stream(FAKE, FAKE, 4, 1, 1, 8, None) == INVALID
     assert L.ep_probe_stream(FAKE, FAKE, 4, 1, 1, -1, None) == INVALID
     assert L.ep_probe_stream(None, FAKE, 4, 1, 1, 0, None) == INVALID
     assert L.ep_probe_stream(FAKE + 8, FAKE, 4, 1, 1, 0, None) == MISALIGNED
     assert L.ep_probe_stream(FAKE, FAKE + 4, 4, 1, 1, 0, None) == MISALIGNED
-    assert L.ep_probe_stream(None, None, 0, 16, 64, 3, None) == OK
+    assert L.ep_probe_stream(None, None, 0, 16, 64, 7, None) == OK
 
 
 def test_binding_rejects_host_tensors():

@@ -10,7 +10,7 @@ from test_gpu_parity import DEV, log, setup_module  # noqa: F401
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("policy", [0, 1, 2, 3])
+@pytest.mark.parametrize("policy", [0, 1, 2, 3, 4, 7])
 @pytest.mark.parametrize("units,r,w", [(1, 1, 1), (5, 4, 3), (37, 16, 2), (9, 2, 8), (3, 8, 64)])
 def test_probe_stream_contract(units, r, w, policy):
     log(f"[probe] units={units} r={r} w={w} policy={policy}")

@@ -197,3 +197,38 @@ def test_quantise_then_passthrough_equals_fp8_dispatch():
     ep.ep_dispatch(shape, x, slot, ep.EP_FP8_E4M3, rq2, rs2)
     torch.cuda.synchronize()
     assert torch.equal(rq1, rq2) and torch.equal(rs1, rs2)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp8", "mxfp4", "prequantized"])
+def test_streaming_launch_with_unequal_xcd_eighths(fmt):
+    """Whole-GPU dispatches above 64 MiB of row traffic take their workgroups in XCD-contiguous order (each of
+    the 8 XCDs one contiguous eighth).  Here the workgroup count is not a multiple of 8 (2062, 4126 or 1031
+    workgroups), so the eighths differ in size: every held row still matches the oracle and no other row is
+    written."""
+    T = 2063 if fmt == "mxfp4" else 1031
+    H, k, E, R = 8192, 8, 256, 8
+    log(f"[xcd-order] {fmt} T={T}")
+    w = wl.custom(f"xcd_{fmt}", T, H, E, R, k, seed=93)
+    shape = shape_of(w)
+    rng = np.random.default_rng(93)
+    lay = oracle.layout(_idx(rng, T, k, E, 0.05), E, R)
+    held = lay.src_pair >= 0
+    if fmt in ("mxfp8", "mxfp4"):
+        check_mx(w, wl.normal_bf16(93, 0, T, H), lay, 8 if fmt == "mxfp8" else 4)
+    elif fmt == "fp8":
+        x = wl.normal_bf16(93, 0, T, H)
+        rq = torch.full((w.recv_rows, H), 0x5A, dtype=torch.uint8, device=DEV)
+        rs = torch.full((w.recv_rows, H // 128), -1.0, dtype=torch.float32, device=DEV)
+        ep.ep_dispatch(shape, dev_bf16(x), dev_i32(lay.slot), ep.EP_FP8_E4M3, rq, rs)
+        torch.cuda.synchronize()
+        wq, ws = oracle.dispatch_fp8(x, lay.slot, w.recv_rows)
+        q, s = rq.cpu().numpy(), rs.cpu().numpy()
+        assert np.array_equal(q[held], wq[held]) and np.array_equal(s[held], ws[held])
+        assert (q[~held] == 0x5A).all() and (s[~held] == -1.0).all()
+    else:
+        xq = rng.integers(0, 256, (T, H), dtype=np.uint8)
+        xs = rng.standard_normal((T, H // 128)).astype(np.float32)
+        q, s = run_prequantized(shape, xq, xs, lay.slot)
+        wq, ws = oracle.dispatch_prequantized(xq, xs, lay.slot, w.recv_rows)
+        assert np.array_equal(q[held], wq[held]) and np.array_equal(s[held], ws[held])
+        assert (q[~held] == 0x5A).all() and (s[~held] == -1.0).all()

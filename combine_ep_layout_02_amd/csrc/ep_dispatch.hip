@@ -8,9 +8,9 @@
 // combine).  This is one GPU's share: the receive buffer is local HBM.
 //
 // Work unit: one wavefront per slice of a token's row: two 512-column chunks
-// (1024 columns) in a whole-GPU launch; whole rows of up to kMaxChunks
-// chunks in a launch limited to a CU budget, whose persistent wavefronts
-// loop.  Lane l owns columns [512c + 8l, +8) of every chunk c, so each
+// (1024 columns; one chunk for BF16 copies) in a whole-GPU launch; whole
+// rows of up to kMaxChunks chunks in a launch limited to a CU budget, whose
+// persistent wavefronts loop.  Lane l owns columns [512c + 8l, +8) of every chunk c, so each
 // 16-byte load of the wavefront is a fully coalesced 1 KiB read.  The
 // wavefront reads its slice once, keeps it in registers (quantised, for FP8)
 // and then writes it to each of the token's k receive rows.  Measured at
@@ -453,8 +453,19 @@ DispatchSplit dispatch_split(const RowParams& p) {
 
 hipError_t launch_dispatch_bf16(const RowParams& p, hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
-  const DispatchSplit s = dispatch_split(p);
+  DispatchSplit s = dispatch_split(p);
   const bool streaming = (int64_t)p.T * p.k * p.H * 2 >= kStreamingBytes;
+  if (!s.budget) {
+    // BF16 copies have no 128-column blocks to pair up: a whole-GPU launch
+    // takes one-chunk slices (512 columns, 1 KiB per copy).  Measured against
+    // two-chunk slices: 184.7 vs 188.9 us at 8192 tokens x 7168 x top-8,
+    // 39.8 vs 41.6 at 4096 x 4096 x top-6.
+    s.cpw = 1;
+    s.wpt = s.nchunks;
+    s.blocks = (int)(((int64_t)p.T * s.wpt + kWavesPerBlock - 1) / kWavesPerBlock);
+    launch_bf16_nc<1>(s, p, streaming, stream);
+    return hipGetLastError();
+  }
   EP_BY_CAPACITY(launch_bf16_nc, s, p, streaming, stream);
   return hipGetLastError();
 }

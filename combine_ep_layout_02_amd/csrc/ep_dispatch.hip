@@ -44,19 +44,21 @@ constexpr int kWavesPerBlock = 4;  // 256 threads (whole-GPU launches)
 // Slices are handed out grid-stride: a whole-GPU launch has one wavefront per
 // slice and runs the loop once; a launch limited to a CU budget runs that many
 // persistent workgroups, each wavefront taking every (grid * WPB)-th
-// slice.  The loop starts at workgroup index `blk` (the hardware index, or
-// its XCD-contiguous renumbering below).
+// slice.  The loop starts at workgroup index `blk`: the hardware index, or
+// its XCD-contiguous renumbering (first_block, below).
 #define EP_FOR_EACH_SLICE(WPB, total, wave, blk)                                     \
   for (int wave = uniform((blk) * (WPB) + (int)(threadIdx.x >> 6)); wave < (total); \
        wave += (int)gridDim.x * (WPB))
 
 // xcd_contiguous (ep_device.hpp) gives XCD x one contiguous eighth of the
-// slices instead of every eighth workgroup.  Measured at 8192 tokens x 7168, whole-GPU launches: FP8 93.2-93.7 vs
-// 100.3-100.7 us, MXFP8 92.6 vs 100.4, MXFP4 55.7 vs 57.6, and FP8 at 4096 x
-// 4096 x top-6 23.5 vs 24.1; runs of 16 to 256 workgroups per XCD instead of
-// one eighth gain little or nothing.  It is applied to the formats with
-// block scales: BF16 dispatch (188.0 vs 188.4 us; 42.4 vs 41.5 at 4096 x
-// 4096), combine (187.9 vs 175.3) and decode-sized launches do not gain.
+// slices instead of every eighth workgroup.  Measured at 8192 tokens x 7168
+// in whole-GPU launches: FP8 93.2-93.7 vs 100.3-100.7 us, MXFP8 92.6 vs
+// 100.4, MXFP4 55.7 vs 57.6, and FP8 at 4096 x 4096 x top-6 23.5 vs 24.1;
+// runs of 16 to 256 workgroups per XCD instead of one eighth gain little or
+// nothing.  It is applied to the formats with block scales in whole-GPU
+// launches above the streaming threshold: BF16 dispatch (188.0 vs 188.4 us;
+// 42.4 vs 41.5 at 4096 x 4096), combine (187.9 vs 175.3), decode-sized
+// launches and CU-budget launches do not gain from it.
 __device__ __forceinline__ int first_block(int xcd) {
   return xcd ? xcd_contiguous((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x;
 }

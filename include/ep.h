@@ -199,6 +199,10 @@ ep_status_t ep_layout(const ep_shape_t *shape, const int32_t *topk_idx,
  *   recv_scale fp32 [ep_recv_rows, H/128] for EP_FP8_E4M3, uint8
  *              [ep_recv_rows, H/32] for the MX formats; ignored (may be
  *              NULL) for EP_BF16
+ *
+ * Non-finite x: BF16 copies any bits.  An EP_FP8_E4M3 block holding an Inf
+ * gets an Inf scale, its finite elements code to +-0 and the Inf to a NaN
+ * code; the codes and scale of a block holding a NaN are unspecified.
  */
 ep_status_t ep_dispatch(const ep_shape_t *shape, const void *x, const int32_t *slot,
                         ep_dtype_t recv_dtype, void *recv_x, void *recv_scale,
@@ -249,7 +253,8 @@ ep_status_t ep_dispatch_prequantized(const ep_shape_t *shape, const void *x_q,
  *   out[t, h] = BF16_RNE( acc ),  acc = +0, then for j = 0..k-1 with
  *               slot[t, j] >= 0:  acc = fmaf(w[t, j], y[slot[t, j], h], acc)
  * The fixed order makes the result deterministic and identical to a scalar
- * evaluation of the same chain.
+ * evaluation of the same chain.  Non-finite y follows IEEE arithmetic; a
+ * NaN result's bit pattern is not specified.
  *
  *   y             BF16 [ep_recv_rows, H]   expert outputs in receive layout
  *   slot          int32 [T, k]             from ep_layout

@@ -324,6 +324,9 @@ void oracle_dispatch_fp8(int64_t T, int64_t H, int64_t k,
         for (b = 0; b < nb; ++b) {
             const uint16_t *xb = x + t * H + b * 128;
             float amax = 0.0f, s;
+            /* a NaN never compares greater, so it takes no part in amax (a
+             * block holding one is outside the GPU path's contract); an Inf
+             * makes the scale Inf */
             for (i = 0; i < 128; ++i) {
                 float a = fabsf(bf16_to_f32(xb[i]));
                 if (a > amax) amax = a;

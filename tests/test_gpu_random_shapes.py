@@ -7,7 +7,9 @@ capacity may drop pairs.  Each draw runs ep_layout, ep_layout_dispatch, BF16 / F
 pre-quantised dispatch, combine and the backward pair through the C ABI and compares every output with the
 oracle (bit for bit; grad_weights within its stated bound); every fourth draw repeats dispatch, combine
 and the backward pair under a CU budget (persistent workgroups), which must give the same bytes.  Inputs
-come from the seeded generators only.
+come from the seeded generators only.  Eight more draws sit above the 64 MiB streaming threshold (up to 3300
+tokens, 5120 to 8192 columns, k = 3 to 8, flat and padded layouts), where the large-batch code paths run: layout,
+FP8 and BF16 dispatch and combine, each compared in full.
 """
 import dataclasses
 
@@ -162,3 +164,62 @@ def test_random_shape(seed):
         assert np.array_equal(bq.view(torch.uint8).cpu().numpy()[held], wq[held])
         assert np.array_equal(bs.cpu().numpy()[held], ws[held])
         assert torch.equal(bout, out) and torch.equal(bgx, gx) and torch.equal(bgy, gy) and torch.equal(bgw, gw)
+
+
+NLARGE = 8
+
+
+def draw_large(seed):
+    """A random shape above the 64 MiB streaming threshold (the large-batch code paths: non-temporal row
+    traffic, XCD-contiguous dispatch order, two-group combine items)."""
+    rng = np.random.default_rng([seed, 779])
+    E = int(rng.choice([64, 128, 256]))
+    R = int(rng.choice([d for d in (1, 2, 4, 8) if E % d == 0]))
+    k = int(rng.choice([3, 4, 6, 8]))
+    H = 128 * int(rng.integers(40, 65))           # 5120 .. 8192 columns, not always a multiple of 1024
+    T = int(np.ceil((64 << 20) / (k * H))) + int(rng.integers(0, 1500))
+    C = int(rng.integers(T * k // E, 2 * T * k // E)) if rng.random() < 0.25 else 0
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    idx[rng.random(idx.shape) < 0.05] = -1
+    weights = rng.standard_normal((T, k)).astype(np.float32)
+    return dict(T=T, H=H, k=k, E=E, R=R, C=C, idx=idx, weights=weights)
+
+
+@pytest.mark.parametrize("seed", range(NLARGE))
+def test_random_streaming_shape(seed):
+    d = draw_large(seed)
+    T, H, k, E, R, C = (d[n] for n in ("T", "H", "k", "E", "R", "C"))
+    log(f"[random-large {seed}] T={T} H={H} k={k} E={E} R={R} C={C}")
+    shape = ep.EpShape(T, H, k, E, R, 1, C)
+    rows = ep.ep_recv_rows(shape)
+    lay = oracle.layout(d["idx"], E, R, 1, C)
+    held = lay.src_pair >= 0
+    x = wl.normal_bf16(seed, 0, T, H)
+    y = wl.normal_bf16(seed, 2, rows, H)
+    bufs = ep.LayoutBuffers.allocate(shape, DEV)
+    bufs.run(dev_i32(d["idx"]))
+    torch.cuda.synchronize()
+    assert_layout_equal(bufs, lay)
+    slot = bufs.slot
+
+    rq, rs = ep.alloc_recv(shape, ep.EP_FP8_E4M3, DEV)
+    fill_u8(rq, 0x5A)
+    ep.ep_dispatch(shape, dev_bf16(x), slot, ep.EP_FP8_E4M3, rq, rs)
+    torch.cuda.synchronize()
+    wq, ws = oracle.dispatch_fp8(x, lay.slot, rows)
+    got_q = rq.view(torch.uint8).cpu().numpy()
+    assert np.array_equal(got_q[held], wq[held]) and np.array_equal(rs.cpu().numpy()[held], ws[held])
+    assert (got_q[~held] == 0x5A).all()
+    del rq, rs, got_q, wq, ws
+
+    rb, _ = ep.alloc_recv(shape, ep.EP_BF16, DEV)
+    ep.ep_dispatch(shape, dev_bf16(x), slot, ep.EP_BF16, rb)
+    torch.cuda.synchronize()
+    assert np.array_equal(rb.view(torch.int16).cpu().numpy().view(np.uint16)[held],
+                          oracle.dispatch_bf16(x, lay.slot, rows)[held])
+    del rb
+
+    out = torch.full((T, H), SENTINEL, dtype=torch.int16, device=DEV)
+    ep.ep_combine(shape, dev_bf16(y), slot, dev_f32(d["weights"]), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u16(out), oracle.combine(y, lay.slot, d["weights"]))

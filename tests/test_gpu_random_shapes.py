@@ -9,7 +9,7 @@ oracle (bit for bit; grad_weights within its stated bound); every fourth draw re
 and the backward pair under a CU budget (persistent workgroups), which must give the same bytes.  Inputs
 come from the seeded generators only.  Eight more draws sit above the 64 MiB streaming threshold (up to 3300
 tokens, 5120 to 8192 columns, k = 3 to 8, flat and padded layouts), where the large-batch code paths run: layout,
-FP8 and BF16 dispatch and combine, each compared in full.
+every dispatch format, combine and the backward pair, each compared in full.
 """
 import dataclasses
 
@@ -223,3 +223,37 @@ def test_random_streaming_shape(seed):
     ep.ep_combine(shape, dev_bf16(y), slot, dev_f32(d["weights"]), out)
     torch.cuda.synchronize()
     assert np.array_equal(host_u16(out), oracle.combine(y, lay.slot, d["weights"]))
+    del out
+
+    # the MX formats and the pre-quantised passthrough
+    for dtype, bits in ((ep.EP_MXFP8_E4M3, 8), (ep.EP_MXFP4_E2M1, 4)):
+        mq, ms = ep.alloc_recv(shape, dtype, DEV)
+        ep.ep_dispatch(shape, dev_bf16(x), slot, dtype, mq, ms)
+        torch.cuda.synchronize()
+        want_q, want_s = oracle.dispatch_mx(x, lay.slot, rows, bits)
+        assert np.array_equal(mq.view(torch.uint8).cpu().numpy()[held], want_q[held]), f"MX{bits} codes"
+        assert np.array_equal(ms.view(torch.uint8).cpu().numpy()[held], want_s[held]), f"MX{bits} scales"
+        del mq, ms, want_q, want_s
+    prng = np.random.default_rng([seed, 780])
+    xq = prng.integers(0, 256, (T, H), dtype=np.uint8)
+    xs = prng.standard_normal((T, H // 128)).astype(np.float32)
+    pq = torch.full((rows, H), 0x5A, dtype=torch.uint8, device=DEV)
+    ps = torch.full((rows, H // 128), -1.0, dtype=torch.float32, device=DEV)
+    ep.ep_dispatch_prequantized(shape, torch.from_numpy(xq).to(DEV), dev_f32(xs), slot, pq, ps)
+    torch.cuda.synchronize()
+    want_pq, want_ps = oracle.dispatch_prequantized(xq, xs, lay.slot, rows)
+    assert np.array_equal(pq.cpu().numpy()[held], want_pq[held]) and np.array_equal(ps.cpu().numpy()[held], want_ps[held])
+    del pq, ps, want_pq, want_ps
+
+    # the backward pair
+    gx = torch.full((T, H), SENTINEL, dtype=torch.int16, device=DEV)
+    ep.ep_dispatch_backward(shape, dev_bf16(y), slot, gx)
+    gy = torch.full((rows, H), SENTINEL, dtype=torch.int16, device=DEV)
+    gw = torch.full((T, k), float("nan"), dtype=torch.float32, device=DEV)
+    ep.ep_combine_backward(shape, dev_bf16(x), dev_bf16(y), slot, dev_f32(d["weights"]), gy, gw)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u16(gx), oracle.dispatch_backward(y, lay.slot))
+    want_gy, want_gw = oracle.combine_backward(x, y, lay.slot, d["weights"], np.full((rows, H), SENTINEL, np.uint16))
+    got_gy = host_u16(gy)
+    assert np.array_equal(got_gy[held], want_gy[held]) and (got_gy[~held] == SENTINEL).all()
+    assert (np.abs(gw.cpu().numpy().astype(np.float64) - want_gw) <= gw_bound(x, y, lay.slot, H)).all()

@@ -13,7 +13,8 @@ Also reported: per-stage kernel times from HIP events recorded around each
 call in a second timed loop (mean, median, p10, p90), the roofline of the
 dominant kernel (combine, HBM-bound), the same step "cold" (each step after
 reading a 1 GiB buffer, so no cache holds its data), the decode-shaped
-workload's microseconds per call, the backward pair's kernel times on the
+workload's microseconds per call, the same step with layout and dispatch as
+one ep_layout_dispatch call, the backward pair's kernel times on the
 same handle, dispatch in every receive format (BF16, FP8, MXFP8, MXFP4,
 pre-quantised FP8), warm and cold step times of the tiny, mid
 and 16K-token skewed workloads, a plain 1 GiB copy and a streaming probe
@@ -619,6 +620,9 @@ def main():
     value = step.bytes * args.steps / (total_ms / 1e3) / 1e9
     stage = time_stages(step, args.steps)
     lay_ms, disp_ms, comb_ms = stage.mean(axis=0)
+    # the same step with layout and dispatch as one call (ep_layout_dispatch)
+    fused_ms, _ = time_steps(step, args.steps, args.warmup, fused=True)
+    fused_us = fused_ms / args.steps * 1e3
     log("[bench] cold steps (1 GiB read before each)")
     flush = ReadFlush(dev)
     cold_step = time_cold(step, 20, flush)
@@ -703,6 +707,9 @@ def main():
         "stage_GBps": {"dispatch": round(bytes_dispatch(w, True) / (disp_ms / 1e3) / 1e9, 1),
                        "combine": round(achieved, 1)},
         "stages_spread_us": {n: spread_us(stage[:, i]) for i, n in enumerate(("layout", "dispatch", "combine"))},
+        "layout_dispatch_call": {"step_us": round(fused_us, 2), "GBps": round(step.bytes / fused_us / 1e3, 1),
+                                 "note": "the same step with ep_layout_dispatch for layout + dispatch, then "
+                                         "ep_combine; at this size it enqueues the layout and dispatch launches"},
         "cold": {"step_us": spread_us(cold_step), "GBps": round(step.bytes / cold_us / 1e3, 1),
                  "pct_of_hbm_peak": round(100 * step.bytes / cold_us / 1e3 / HBM_PEAK_GBS, 2),
                  "stages_us": {n: spread_us(cold_stage[:, i])

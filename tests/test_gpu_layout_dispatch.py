@@ -70,6 +70,8 @@ FUSED_EDGE = [
     ("padded_decode_hot", 128, 7168, 8, 256, 8, 128, 0.0, 0.0),
     ("h16384_slices", 64, 16384, 2, 16, 4, 0, 0.0, 0.0),
     ("k1", 300, 256, 1, 8, 2, 0, 0.0, 0.0),
+    ("all_masked", 100, 512, 6, 64, 8, 0, 1.0, 0.0),
+    ("all_invalid_padded", 128, 7168, 8, 256, 8, 128, 0.0, 1.0),
 ]
 
 

@@ -162,6 +162,10 @@ LAYOUT_EDGE = [
     ("one_expert_per_rank", 2000, 2, 8, 8, 1, 0, 0.0, 0.0, None),
     ("one_expert_multitile", 3000, 1, 1, 1, 1, 0, 0.0, 0.0, None),
     ("one_expert_per_rank_r128", 900, 4, 128, 128, 1, 0, 0.0, 0.0, None),
+    # no valid pair at all: empty segments, every slot -1
+    ("all_masked_one_tile", 100, 4, 16, 4, 1, 0, 1.0, 0.0, None),
+    ("all_masked_multitile_aligned", 3000, 4, 64, 8, 2, 0, 1.0, 0.0, None),
+    ("all_invalid_padded_multitile", 3000, 4, 64, 8, 1, 20, 0.0, 1.0, None),
 ]
 
 
@@ -235,6 +239,7 @@ DISPATCH_EDGE = [
     ("h640_partial_chunk", 200, 640, 2, 8, 2, 1, 0, 0.0),
     ("h9216_two_slices", 40, 9216, 4, 16, 4, 1, 0, 0.05),
     ("h16384_two_slices", 24, 16384, 3, 12, 3, 1, 0, 0.0),
+    ("all_masked", 300, 1024, 4, 16, 4, 1, 0, 1.0),
 ]
 
 
@@ -294,6 +299,8 @@ COMBINE_EDGE = [
     ("k64_generic", 32, 256, 64, 64, 8, 1, 0, 0.0),
     ("padded_drops", 300, 1024, 4, 16, 4, 1, 40, 0.0),
     ("h136", 100, 136, 2, 8, 2, 4, 0, 0.0),
+    ("all_masked", 300, 1024, 4, 16, 4, 1, 0, 1.0),       # every output is +0
+    ("all_masked_padded", 200, 512, 4, 16, 4, 1, 20, 1.0),
 ]
 
 
@@ -310,6 +317,7 @@ def test_combine_edge_cases(case):
     got = run_combine(w, y, lay.slot, wts)
     want = oracle.combine(y, lay.slot, wts)
     assert (bf16_ulp_distance(got, want) == 0).all()
+    assert np.array_equal(got, want)  # bit for bit, signs of zero included
 
 
 def test_combine_k1_unit_weight_is_gather():
